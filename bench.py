@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Throughput of one Medusa tree-verification round on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
+
+A step is one whole round over one batch of synthetic inputs already resident
+in HBM: ``medusa_tree_attn`` (RoPE at P + depth, staged K/V rows, tree
+attention), ``medusa_accept`` (greedy acceptance over fp32 target logits) and
+``medusa_kv_compact`` (winning-path K/V gather), on one stream with no host
+synchronisation.  The tree itself is compiled once on the host before the
+timed region (the buffers are static for a tree shape) and its compile time
+is reported separately.
+
+Each step uses the next of several independent buffer sets (cache, Q, K/V,
+logits, outputs), together larger than the 256 MB Infinity Cache, so the KV
+stream is served from HBM.  Before its round a set's prefix lengths and status
+word are restored (one 20-byte device copy), so every round runs at the same
+context length.
+
+Printed on stdout: one JSON line.  ``value`` = verified tree nodes per second
+over the timed steps (B * N per step).  ``roofline`` rates the attention call
+(the dominant kernel): algorithmic bytes per launch / mean launch time from
+dispatch-recorded HIP events, against 8 TB/s.  ``cpu_baseline`` times the CPU
+oracle on one round of the same workload.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ATTN_SOURCES = ["attn.hip", "attn_mfma.hip", "attn_common.h", "common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_batched.md")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attn_source_hash():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "medusa_tree_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, N, esize):
+    """Bytes the attention call must move: prefix K/V once, Q, K_new/V_new, staged K/V, O."""
+    prefix_kv = 2 * w.B * w.Hkv * w.P * w.d * esize
+    q = o = w.B * N * w.Hq * w.d * esize
+    new_kv = staged = 2 * w.B * N * w.Hkv * w.d * esize
+    return prefix_kv + q + new_kv + staged + o
+
+
+def measured_traffic(src_hash):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE, encoding="utf-8").read()
+    m_hash = re.search(r"kernel source hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"scaled HBM bytes per launch:\s*([0-9]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+        return None
+    return int(m_bytes.group(1))
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime first)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreateWithFlags(ctypes.byref(ev), 0) == 0
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def build_sets(w, x, tree, n_sets, torch, M):
+    import numpy as np
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dcode = M.BF16 if w.dtype == "bf16" else M.F32
+    N = x["N"]
+    dev = lambda a, d=None: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", d)
+    shared = {"depth": dev(tree["depth"]), "mask": dev(tree["tree_mask"].view(np.int64)),
+              "tidx": dev(tree["tree_indices"]), "retrieve": dev(tree["retrieve"])}
+    pristine = dev(np.concatenate([x["prefix_len"], [0]]).astype(np.int32))
+    attn_ws = M.medusa_tree_attn_workspace_size(dcode, w.B, w.Hq, w.Hkv, w.d, N, x["S_max"])
+    acc_ws = M.medusa_accept_workspace_size(w.B, N)
+    sets = []
+    for _ in range(n_sets):
+        s = {"q": dev(x["q"], dt), "kn": dev(x["k_new"], dt), "vn": dev(x["v_new"], dt),
+             "kc": dev(x["k_cache"], dt), "vc": dev(x["v_cache"], dt),
+             "logits": dev(x["logits"]) if x["logits"] is not None else None,
+             "tids": dev(x["target_ids"]) if x["target_ids"] is not None else None,
+             "cand": dev(x["candidates"]), "ctl": pristine.clone()}
+        s["out"] = torch.empty_like(s["q"])
+        s["prefix"], s["status"] = s["ctl"][: w.B], s["ctl"][w.B:]
+        s["attn_ws"] = torch.zeros(max(attn_ws, 16), dtype=torch.uint8, device="cuda")
+        s["acc_ws"] = torch.zeros(acc_ws, dtype=torch.uint8, device="cuda")
+        s["best"] = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+        s["alen"] = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+        s["frontier"] = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+        s["tokens"] = torch.zeros((w.B, tree["path_width"]), dtype=torch.int32, device="cuda")
+        sets.append(s)
+    return shared, pristine, sets
+
+
+def set_bytes(s):
+    return sum(t.numel() * t.element_size() for t in s.values() if hasattr(t, "numel") and t is not None)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+def cpu_baseline(w, x):
+    """The CPU oracle, as it stands, on the same round: every sequence, head and node."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads
+    from oracle import accept as AC
+    from oracle import attention as A
+    from oracle import compact as C
+    from oracle import tree as T
+
+    spec = workloads.tree_spec(w)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ora = (T.compile_tree(spec["paths"], w.num_heads, w.topk) if spec["paths"] is not None
+               else T.compile_greedy(spec["rank_hit"], spec["n_nodes"]))
+        _, sk, sv = A.tree_attention(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                                     x["prefix_len"], ora["depth"], ora["parent"], w.rope_base)
+        res = AC.accept_batch(ora, x["candidates"], logits=x["logits"], target_ids=x["target_ids"])
+        cache = [np.array(x["k_cache"], np.float64), np.array(x["v_cache"], np.float64)]
+        for b in range(w.B):
+            P = int(x["prefix_len"][b])
+            for c, st in zip(cache, (sk, sv)):
+                c[b, :, P:P + x["N"]] = st[b]
+        C.kv_compact(cache, ora["retrieve"], res["best_path"], res["accept_len"], x["prefix_len"], x["N"])
+        dt = time.perf_counter() - t0
+    return {"value": w.B * x["N"] / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+            "sample": (f"one full round of the workload ({w.B} sequences x {x['N']} nodes x {w.Hq} heads "
+                       f"at P={w.P}): tree compile, per-path binary64 attention, greedy accept, "
+                       f"compaction; {dt:.1f} s on 1 thread of {cpu_model()}")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="batched")
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for > 512 MB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the round is measured per GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import medusa_tree_attention_amd as M
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    spec = workloads.tree_spec(w)
+    t0 = time.perf_counter()
+    tree = (M.medusa_tree_compile(w.num_heads, w.topk, paths=spec["paths"]) if spec["paths"] is not None
+            else M.medusa_tree_compile(w.num_heads, w.topk, rank_hit=spec["rank_hit"], n_nodes=spec["n_nodes"]))
+    compile_us = (time.perf_counter() - t0) * 1e6
+    x = workloads.draw_round(w)
+    N = x["N"]
+    torch.cuda.init()
+    shared, pristine, sets = build_sets(w, x, tree, 1, torch, M)
+    per_set = set_bytes(sets[0])
+    n_sets = args.sets or max(2, -(-512 * 2 ** 20 // per_set))
+    shared, pristine, sets = build_sets(w, x, tree, n_sets, torch, M)
+    log(f"[bench] workload={w.name} N={N} sets={n_sets} x {per_set / 2**20:.1f} MiB")
+
+    lib = M.load()
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    dcode = M.BF16 if w.dtype == "bf16" else M.F32
+    nn = tree["n_paths"]
+    width = tree["path_width"]
+    p = lambda t: None if t is None else t.data_ptr()
+
+    # argument tuples built once per set: the timed loop only calls into the library
+    calls = []
+    for s in sets:
+        kc_arr = (ctypes.c_void_p * 1)(s["kc"].data_ptr())
+        vc_arr = (ctypes.c_void_p * 1)(s["vc"].data_ptr())
+        attn = [sptr, dcode, w.B, w.Hq, w.Hkv, w.d, N, p(shared["depth"]), p(shared["mask"]),
+                tree["mask_words"], p(s["prefix"]), p(s["q"]), p(s["kn"]), p(s["vn"]), p(s["kc"]),
+                p(s["vc"]), x["S_max"], float(w.rope_base), p(s["out"]), p(s["attn_ws"]),
+                s["attn_ws"].numel(), p(s["status"])]
+        acc = (sptr, w.B, N, w.vocab if x["logits"] is not None else 0, p(s["logits"]), p(s["tids"]),
+               p(s["cand"]), x["candidates"].shape[1], p(shared["tidx"]), p(shared["retrieve"]), nn,
+               width, p(s["best"]), p(s["alen"]), p(s["tokens"]), p(s["frontier"]), p(s["acc_ws"]),
+               s["acc_ws"].numel(), p(s["status"]), None, None)
+        cmp_ = (sptr, dcode, 1, w.B, w.Hkv, w.d, x["S_max"], N, ctypes.cast(kc_arr, ctypes.c_void_p),
+                ctypes.cast(vc_arr, ctypes.c_void_p), p(shared["retrieve"]), nn, width, p(s["best"]),
+                p(s["alen"]), p(s["prefix"]), p(s["status"]), None, None)
+        calls.append((s, attn, acc, cmp_, kc_arr, vc_arr))
+
+    ev = HipEvents()
+    total = args.warmup + args.steps
+    events = [(ev.create(), ev.create()) for _ in range(total)]
+
+    def step(i):
+        s, attn, acc, cmp_, _, _ = calls[i % n_sets]
+        s["ctl"].copy_(pristine)
+        rc = lib.medusa_tree_attn(*attn, events[i][0], events[i][1])
+        rc |= lib.medusa_accept(*acc)
+        rc |= lib.medusa_kv_compact(*cmp_)
+        if rc:
+            raise RuntimeError(f"library call failed at step {i}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    statuses = [int(s["status"].item()) for s in sets]
+    if any(statuses):
+        raise RuntimeError(f"device status words {statuses}: the round failed")
+    attn_ms = np.array([ev.elapsed_ms(a, b) for a, b in events[args.warmup:]])
+    for a, b in events:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    copy_info = None
+    if args.copy_calibration:
+        src = torch.randn(2 ** 26, device="cuda")      # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        copy_info = "torch.neg over 2^26 fp32 (256 MiB read + 256 MiB written) x5"
+
+    esize = 2 if w.dtype == "bf16" else 4
+    alg = algorithmic_bytes(w, N, esize)
+    mean_s = float(attn_ms.mean()) * 1e-3
+    achieved = alg / mean_s / 1e9
+    src_hash = attn_source_hash()
+    result = {
+        "metric": "tree-verify attention nodes/s and % HBM peak, 64-node tree @ ctx 4096",
+        "value": w.B * N * args.steps / elapsed,
+        "unit": "nodes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": (f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d_h={w.d}, P={w.P}, "
+                                f"N={N} ({w.tree} tree), V={w.vocab}"),
+                   "global_batch": w.B, "seq_len": w.P, "tree_nodes": N, "buffer_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(src_hash),
+                     "kernel": "medusa_tree_attn", "algorithmic_bytes": alg,
+                     "mean_us": mean_s * 1e6, "median_us": float(np.median(attn_ms)) * 1e3,
+                     "p10_us": float(np.percentile(attn_ms, 10)) * 1e3,
+                     "p90_us": float(np.percentile(attn_ms, 90)) * 1e3,
+                     "source_hash": src_hash},
+        "tree_compile_us": compile_us,
+    }
+    if copy_info:
+        result["copy_calibration"] = copy_info
+    log(f"[bench] attention mean {mean_s * 1e6:.2f} us -> {achieved:.0f} GB/s "
+        f"({achieved / HBM_PEAK_GBS:.1%} of HBM peak); step {elapsed / args.steps * 1e6:.1f} us")
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on one round ...")
+        result["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,43 @@
+// Arguments and checks shared by the tree-attention device paths.
+#pragma once
+
+#include <cstdint>
+
+#include "common.h"
+
+namespace medusa {
+
+struct AttnArgs {
+  const int32_t* depth;        // [N]
+  const uint64_t* mask;        // [N][mask_words]
+  const int32_t* prefix_len;   // [B]
+  const void* q;               // [B][N][Hq][D]
+  const void* k_new;           // [B][N][Hkv][D]
+  const void* v_new;           // [B][N][Hkv][D]
+  void* k_cache;               // [B][Hkv][S_max][D]
+  void* v_cache;               // [B][Hkv][S_max][D]
+  void* out;                   // [B][N][Hq][D]
+  int32_t* status;
+  void* workspace;
+  double rope_base;
+  int32_t B, Hq, Hkv, N, mask_words, S_max;
+};
+
+// Every sequence's staged rows [P_b, P_b + N) must lie inside the cache.  All
+// blocks evaluate the same condition, so they all store or none does.
+__device__ __forceinline__ bool prefixes_fit(const AttnArgs& a) {
+  bool ok = true;
+  for (int b = 0; b < a.B; ++b) {
+    const int64_t P = a.prefix_len[b];
+    ok = ok && P >= 0 && P + a.N <= a.S_max;
+  }
+  return ok;
+}
+
+// Host-side dispatch helpers implemented next to the MFMA kernel.
+bool mfma_path_applies(medusa_dtype dt, int32_t Hq, int32_t Hkv, int32_t d_h, int32_t N);
+size_t attn_workspace_bytes(medusa_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d_h,
+                            int32_t N, int32_t S_max);
+medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev_stop);
+
+}  // namespace medusa

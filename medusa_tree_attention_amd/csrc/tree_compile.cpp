@@ -1,0 +1,211 @@
+// Host tree compiler: rank paths (explicit, or grown greedily from rank-hit
+// probabilities) -> the flattened buffers every round reads.
+//
+// [M7.2] = "M7.2 - Medusa: Multi-Head Candidates, Tree Attention, and Verification"
+//   §0x04A "Sparse Tree Construction": prefix closure; canonical row order by
+//     (length, path); candidate gather slot 1 + (len-1)*TOPK + last rank;
+//     ancestry mask; depth; maximal retrieve rows with a negative sentinel.
+//   §0x04B "Calibration Probabilities And Expected Accepted Length": the path
+//     weight is the product of the per-depth exact-rank hit probabilities.
+//   §0x04C "Greedy Frontier Search And Its Boundary": admit the best frontier
+//     path whose parent is present until the budget is spent.
+// "Medusa Part II: Candidate Trees, Verification, and Acceptance", Part 3
+//   Step 3, describes the same budgeted growth.
+//
+// This is integer work plus binary64 products; it runs once per tree shape on
+// the host (the pages build these buffers at start-up and keep them resident).
+// Built with -ffp-contract=off so every weight is the plain left-to-right
+// product of IEEE binary64 multiplications.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <queue>
+#include <vector>
+
+#include "medusa.h"
+
+namespace {
+
+constexpr int32_t kMaxNodes = 16384;  // mask alone is N*N/8 bytes (32 MiB here)
+
+using Path = std::vector<int32_t>;
+
+struct Frontier {
+  double w;
+  Path p;
+};
+
+// Priority of the greedy loop: larger weight first, then the shorter path,
+// then the lexicographically smaller one.
+struct LowerPriority {
+  bool operator()(const Frontier& a, const Frontier& b) const {
+    if (a.w != b.w) return a.w < b.w;
+    if (a.p.size() != b.p.size()) return a.p.size() > b.p.size();
+    return a.p > b.p;
+  }
+};
+
+bool canonical_less(const Path& a, const Path& b) {
+  if (a.size() != b.size()) return a.size() < b.size();
+  return a < b;
+}
+
+// Number of rank tuples of length 1..K, saturated at `cap`.
+int64_t tuple_count(int32_t K, int32_t topk, int64_t cap) {
+  int64_t total = 0, level = 1;
+  for (int32_t d = 0; d < K; ++d) {
+    level = (level > cap / topk) ? cap : level * topk;
+    total = std::min<int64_t>(cap, total + level);
+  }
+  return total;
+}
+
+medusa_status grow_greedy(const medusa_tree_spec& s, std::vector<Path>& paths) {
+  const int32_t K = s.num_heads, topk = s.topk;
+  for (int64_t i = 0; i < int64_t(K) * topk; ++i) {
+    const double a = s.rank_hit[i];
+    if (!(a >= 0.0 && a <= 1.0)) return MEDUSA_EINVAL;  // also rejects NaN
+  }
+  if (s.n_nodes < 1) return MEDUSA_EINVAL;
+  if (s.n_nodes > kMaxNodes) return MEDUSA_ECAPACITY;
+  const int64_t budget = int64_t(s.n_nodes) - 1;
+  if (budget > tuple_count(K, topk, int64_t(1) << 40)) return MEDUSA_ECAPACITY;
+
+  std::priority_queue<Frontier, std::vector<Frontier>, LowerPriority> frontier;
+  for (int32_t r = 0; r < topk; ++r) frontier.push({1.0 * s.rank_hit[r], Path{r}});
+  while (int64_t(paths.size()) < budget) {
+    Frontier best = frontier.top();
+    frontier.pop();
+    const int32_t depth = int32_t(best.p.size());
+    if (depth < K) {
+      for (int32_t r = 0; r < topk; ++r) {
+        Path child = best.p;
+        child.push_back(r);
+        frontier.push({best.w * s.rank_hit[int64_t(depth) * topk + r], std::move(child)});
+      }
+    }
+    paths.push_back(std::move(best.p));
+  }
+  return MEDUSA_OK;
+}
+
+medusa_status read_explicit(const medusa_tree_spec& s, std::vector<Path>& paths) {
+  if (s.n_paths < 0) return MEDUSA_EINVAL;
+  if (s.n_paths >= kMaxNodes) return MEDUSA_ECAPACITY;
+  if (s.n_paths > 0 && s.path_ranks == nullptr) return MEDUSA_EINVAL;
+  int64_t off = 0;
+  for (int32_t i = 0; i < s.n_paths; ++i) {
+    const int32_t len = s.path_len[i];
+    if (len < 1 || len > s.num_heads) return MEDUSA_EINVAL;
+    Path p(s.path_ranks + off, s.path_ranks + off + len);
+    off += len;
+    for (int32_t r : p)
+      if (r < 0 || r >= s.topk) return MEDUSA_EINVAL;
+    paths.push_back(std::move(p));
+  }
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
+extern "C" medusa_status medusa_tree_compile(const medusa_tree_spec* spec, medusa_tree* out) {
+  if (spec == nullptr || out == nullptr) return MEDUSA_EINVAL;
+  const medusa_tree_spec& s = *spec;
+  if (s.num_heads < 1 || s.topk < 1 || s.num_heads > 64) return MEDUSA_EINVAL;
+
+  std::vector<Path> paths;
+  medusa_status st;
+  if (s.path_len != nullptr) {
+    st = read_explicit(s, paths);
+  } else {
+    if (s.rank_hit == nullptr) return MEDUSA_EINVAL;
+    st = grow_greedy(s, paths);
+  }
+  if (st != MEDUSA_OK) return st;
+
+  // canonical order, duplicates, prefix closure
+  std::sort(paths.begin(), paths.end(), canonical_less);
+  std::map<Path, int32_t> row;
+  row[Path{}] = 0;
+  for (size_t i = 0; i < paths.size(); ++i) {
+    if (!row.emplace(paths[i], int32_t(i + 1)).second) return MEDUSA_EINVAL;
+  }
+  const int32_t n = int32_t(paths.size()) + 1;
+  std::vector<int32_t> parent(n, -1), depth(n, 0), slot(n, 0);
+  for (int32_t u = 1; u < n; ++u) {
+    const Path& p = paths[u - 1];
+    Path pre(p.begin(), p.end() - 1);
+    auto it = row.find(pre);
+    if (it == row.end()) return MEDUSA_ENOT_PREFIX_CLOSED;
+    parent[u] = it->second;
+    depth[u] = int32_t(p.size());
+    slot[u] = 1 + (depth[u] - 1) * s.topk + p.back();
+  }
+  std::vector<char> has_child(n, 0);
+  for (int32_t u = 1; u < n; ++u) has_child[parent[u]] = 1;
+  std::vector<int32_t> leaves;
+  int32_t max_depth = 0;
+  for (int32_t u = 0; u < n; ++u) {
+    if (!has_child[u]) leaves.push_back(u);
+    max_depth = std::max(max_depth, depth[u]);
+  }
+  const int32_t words = (n + 63) / 64;
+  const int32_t width = max_depth + 1;
+  const int32_t n_leaves = int32_t(leaves.size());
+
+  const bool query = out->tree_indices == nullptr && out->depth == nullptr &&
+                     out->parent == nullptr && out->tree_mask == nullptr &&
+                     out->retrieve_indices == nullptr && out->node_weight == nullptr;
+  if (query) {
+    out->n_nodes = n;
+    out->n_paths = n_leaves;
+    out->path_width = width;
+    out->mask_words = words;
+    return MEDUSA_OK;
+  }
+  if (out->tree_indices == nullptr || out->depth == nullptr || out->parent == nullptr ||
+      out->tree_mask == nullptr || out->retrieve_indices == nullptr)
+    return MEDUSA_EINVAL;
+  if (out->n_nodes < n || out->n_paths < n_leaves || out->path_width < width ||
+      out->mask_words < words)
+    return MEDUSA_EBUFSIZE;
+  if (out->node_weight != nullptr && s.rank_hit == nullptr) return MEDUSA_EINVAL;
+  if (out->node_weight != nullptr) {
+    for (int64_t i = 0; i < int64_t(s.num_heads) * s.topk; ++i)
+      if (!(s.rank_hit[i] >= 0.0 && s.rank_hit[i] <= 1.0)) return MEDUSA_EINVAL;
+  }
+
+  // every check passed: emit
+  for (int32_t u = 0; u < n; ++u) {
+    out->tree_indices[u] = slot[u];
+    out->depth[u] = depth[u];
+    out->parent[u] = parent[u];
+  }
+  std::memset(out->tree_mask, 0, sizeof(uint64_t) * size_t(n) * size_t(words));
+  for (int32_t u = 0; u < n; ++u) {
+    uint64_t* m = out->tree_mask + size_t(u) * words;
+    for (int32_t v = u; v >= 0; v = parent[v]) m[v / 64] |= uint64_t(1) << (v % 64);
+  }
+  for (int32_t i = 0; i < n_leaves; ++i) {
+    int32_t* r = out->retrieve_indices + size_t(i) * width;
+    std::fill(r, r + width, -1);
+    for (int32_t v = leaves[i]; v >= 0; v = parent[v]) r[depth[v]] = v;
+  }
+  if (out->node_weight != nullptr) {
+    out->node_weight[0] = 1.0;
+    for (int32_t u = 1; u < n; ++u) {
+      const Path& p = paths[u - 1];
+      double w = 1.0;
+      for (size_t j = 0; j < p.size(); ++j) w = w * s.rank_hit[int64_t(j) * s.topk + p[j]];
+      out->node_weight[u] = w;
+    }
+  }
+  out->n_nodes = n;
+  out->n_paths = n_leaves;
+  out->path_width = width;
+  out->mask_words = words;
+  return MEDUSA_OK;
+}

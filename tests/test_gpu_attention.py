@@ -1,0 +1,108 @@
+"""Tree attention on the GPU against the binary64 oracle (through the C ABI)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_support import TOL, AttnRun, announce, compile_both, host, sample_rows  # noqa: E402
+
+
+def _all_rows(w, N):
+    return [(b, u, h) for b in range(w.B) for u in range(N) for h in range(w.Hq)]
+
+
+@pytest.mark.parametrize("name,n_rows", [("tiny", None), ("llama7b", None), ("gqa8b", 192),
+                                         ("wide", 192), ("batched", 256)])
+def test_workload_attention(name, n_rows):
+    w = workloads.WORKLOADS[name]
+    announce(f"attention workload={name}")
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w)
+    N = x["N"]
+    run = AttnRun(w, x, ora)
+    assert run.run() == 0
+    if n_rows is None:
+        rows = _all_rows(w, N)
+    else:
+        # always include the root, the deepest rows, first and last heads, every sequence
+        must = [(b, u, h) for b in range(w.B) for u in (0, N - 1) for h in (0, w.Hq - 1)]
+        rows = sample_rows(w, N, n_rows, seed=1, must=must)
+    err, staged = run.check(rows)
+    announce(f"  max abs err {err:.3e}, staged-row error {staged:.3f} ulp-bound")
+    assert err <= TOL[w.dtype]
+    assert staged <= 1.0
+
+
+EDGE = {
+    # root-only tree, an empty prefix next to a ragged one
+    "root_only_f32": (dataclasses.replace(workloads.WORKLOADS["tiny"], B=2, tree="greedy",
+                                          n_nodes=1, d=64), [0, 77]),
+    "root_only_bf16": (dataclasses.replace(workloads.WORKLOADS["llama7b"], B=2, Hq=4, Hkv=2,
+                                           n_nodes=1), [0, 130]),
+    # ragged prefixes not multiple of 64, GQA group 4, small tree
+    "ragged_gqa": (dataclasses.replace(workloads.WORKLOADS["batched"], B=3, Hq=8, Hkv=2,
+                                       tree="cartesian", branching=(2, 2), num_heads=2, topk=2,
+                                       slack=5), [1, 64, 200]),
+    # d_h = 64 in bf16, mask spanning two words (N = 100)
+    "d64_two_words": (dataclasses.replace(workloads.WORKLOADS["llama7b"], B=2, Hq=4, Hkv=1, d=64,
+                                          n_nodes=100), [37, 300]),
+    # a chain: ordinary causal attention over prefix + path
+    "chain_f32": (dataclasses.replace(workloads.WORKLOADS["tiny"], Hq=2, Hkv=1, d=128,
+                                      branching=(1, 1, 1, 1), num_heads=4, topk=1), [65]),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+def test_edge_cases(case):
+    w, P = EDGE[case]
+    announce(f"attention edge case={case}")
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w, seed=11, prefix_len=P)
+    run = AttnRun(w, x, ora)
+    assert run.run() == 0
+    err, staged = run.check(_all_rows(w, x["N"]))
+    assert err <= TOL[w.dtype] and staged <= 1.0
+
+
+def test_capacity_violation_stores_nothing():
+    w = dataclasses.replace(workloads.WORKLOADS["tiny"], B=2)
+    announce("attention capacity violation")
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w, seed=3, prefix_len=[10, 128])
+    x["prefix_len"] = np.array([10, 129], np.int32)   # 129 + 7 > S_max = 135
+    run = AttnRun(w, x, ora)
+    kc0, out0 = host(run.kc).copy(), host(run.out).copy()
+    assert run.run() == -3
+    assert np.array_equal(host(run.kc), kc0) and np.array_equal(host(run.out), out0)
+
+
+def test_sticky_status_skips_the_call():
+    w = workloads.WORKLOADS["tiny"]
+    announce("attention with a failed round")
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w)
+    run = AttnRun(w, x, ora, status_init=-1)
+    kc0, out0 = host(run.kc).copy(), host(run.out).copy()
+    assert run.run() == -1
+    assert np.array_equal(host(run.kc), kc0) and np.array_equal(host(run.out), out0)
+
+
+def test_host_rejects_bad_shapes():
+    import medusa_tree_attention_amd as M
+    w = workloads.WORKLOADS["tiny"]
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w)
+    run = AttnRun(w, x, ora)
+    bad_q = torch.zeros((1, 7, 1, 96), device="cuda")
+    with pytest.raises(M.MedusaError) as e:
+        M.medusa_tree_attn(bad_q, run.kn, run.vn, run.kc, run.vc, run.td["depth"], run.td["mask"],
+                           run.prefix, 1e4, bad_q, run.ws, run.status)
+    assert e.value.name == "MEDUSA_EUNSUPPORTED"
