@@ -27,7 +27,7 @@ def test_workload_attention(name, n_rows):
     lib, ora = compile_both(w)
     x = workloads.draw_round(w)
     N = x["N"]
-    run = AttnRun(w, x, ora)
+    run = AttnRun(w, x, lib, ora)
     assert run.run() == 0
     if n_rows is None:
         rows = _all_rows(w, N)
@@ -66,7 +66,7 @@ def test_edge_cases(case):
     announce(f"attention edge case={case}")
     lib, ora = compile_both(w)
     x = workloads.draw_round(w, seed=11, prefix_len=P)
-    run = AttnRun(w, x, ora)
+    run = AttnRun(w, x, lib, ora)
     assert run.run() == 0
     err, staged = run.check(_all_rows(w, x["N"]))
     assert err <= TOL[w.dtype] and staged <= 1.0
@@ -78,7 +78,7 @@ def test_capacity_violation_stores_nothing():
     lib, ora = compile_both(w)
     x = workloads.draw_round(w, seed=3, prefix_len=[10, 128])
     x["prefix_len"] = np.array([10, 129], np.int32)   # 129 + 7 > S_max = 135
-    run = AttnRun(w, x, ora)
+    run = AttnRun(w, x, lib, ora)
     kc0, out0 = host(run.kc).copy(), host(run.out).copy()
     assert run.run() == -3
     assert np.array_equal(host(run.kc), kc0) and np.array_equal(host(run.out), out0)
@@ -89,7 +89,7 @@ def test_sticky_status_skips_the_call():
     announce("attention with a failed round")
     lib, ora = compile_both(w)
     x = workloads.draw_round(w)
-    run = AttnRun(w, x, ora, status_init=-1)
+    run = AttnRun(w, x, lib, ora, status_init=-1)
     kc0, out0 = host(run.kc).copy(), host(run.out).copy()
     assert run.run() == -1
     assert np.array_equal(host(run.kc), kc0) and np.array_equal(host(run.out), out0)
@@ -100,7 +100,7 @@ def test_host_rejects_bad_shapes():
     w = workloads.WORKLOADS["tiny"]
     lib, ora = compile_both(w)
     x = workloads.draw_round(w)
-    run = AttnRun(w, x, ora)
+    run = AttnRun(w, x, lib, ora)
     bad_q = torch.zeros((1, 7, 1, 96), device="cuda")
     with pytest.raises(M.MedusaError) as e:
         M.medusa_tree_attn(bad_q, run.kn, run.vn, run.kc, run.vc, run.td["depth"], run.td["mask"],

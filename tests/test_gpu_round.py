@@ -29,7 +29,7 @@ def test_round(name):
         tokens = x["candidates"][b][ora["tree_indices"]]
         workloads.plant_acceptance(rng, x, tokens, ora["retrieve"], ora["parent"], b, path, real)
 
-    att = AttnRun(w, x, lib)
+    att = AttnRun(w, x, lib, ora)
     td = att.td
     outs = {k: torch.zeros(s, dtype=torch.int32, device="cuda") for k, s in
             [("best_path", (w.B,)), ("accept_len", (w.B,)),
