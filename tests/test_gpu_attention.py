@@ -54,6 +54,13 @@ EDGE = {
     # d_h = 64 in bf16, mask spanning two words (N = 100)
     "d64_two_words": (dataclasses.replace(workloads.WORKLOADS["llama7b"], B=2, Hq=4, Hkv=1, d=64,
                                           n_nodes=100), [37, 300]),
+    # matrix-core path with many prefix splits, an empty prefix, splits with no keys,
+    # a split count that breaks the XCD grouping, and two staged tiles
+    "mfma_splits_ragged": (dataclasses.replace(workloads.WORKLOADS["batched"], B=3, Hq=8, Hkv=2),
+                           [0, 700, 3001]),
+    # matrix-core path with a query block that is not a multiple of 64 rows (N * group = 20)
+    "mfma_partial_qtile": (dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=4, Hkv=1,
+                                               n_nodes=5), [257, 31]),
     # a chain: ordinary causal attention over prefix + path
     "chain_f32": (dataclasses.replace(workloads.WORKLOADS["tiny"], Hq=2, Hkv=1, d=128,
                                       branching=(1, 1, 1, 1), num_heads=4, topk=1), [65]),
@@ -106,3 +113,20 @@ def test_host_rejects_bad_shapes():
         M.medusa_tree_attn(bad_q, run.kn, run.vn, run.kc, run.vc, run.td["depth"], run.td["mask"],
                            run.prefix, 1e4, bad_q, run.ws, run.status)
     assert e.value.name == "MEDUSA_EUNSUPPORTED"
+
+
+def test_repeated_calls_reuse_the_workspace():
+    """The split-merge counters live in the workspace and must be left at zero by every call."""
+    w = workloads.WORKLOADS["batched"]
+    announce("attention twice on one workspace")
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w, seed=21)
+    run = AttnRun(w, x, lib, ora)
+    assert run.run() == 0
+    first = run.out.clone()
+    run.out.fill_(3.0)
+    run.kc.copy_(torch.from_numpy(x["k_cache"]).to("cuda", torch.bfloat16))
+    assert run.run() == 0
+    assert torch.equal(first, run.out)
+    counters = run.ws[:512].cpu().numpy()   # 4 bytes x 32 units x 4 q-tiles
+    assert (counters == 0).all()
