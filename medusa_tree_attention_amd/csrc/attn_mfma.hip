@@ -12,19 +12,24 @@
 //    against a key tile is a dense contraction, so both products run on
 //    v_mfma_f32_32x32x16_bf16.
 //  * A workgroup takes 64 query rows (a q-tile) and one contiguous split of
-//    the committed prefix.  Its four wavefronts hold the same 64 rotated,
-//    pre-scaled query rows in registers and take interleaved 32-key tiles of
-//    the split; the last split also takes the staged rows.  The q-tiles of
-//    one split are launched onto one XCD (block id modulo 8) so that their
-//    identical KV stream is served once from that XCD's L2.
-//  * Scores are formed transposed, S^T = K Q^T (K rows are the A operand, read
-//    from LDS with 16-byte reads), so the probability tile comes out of the
-//    accumulator already in the B-operand layout of O^T = V^T P^T; V^T is read
-//    from LDS with the transposing ds_read_b64_tr_b16.  No shuffle of P.
+//    the committed prefix; the last split also takes the staged rows.  Its
+//    four wavefronts hold the same 64 rotated, pre-scaled query rows in
+//    registers and each streams its own interleaved 32-key tiles, so the main
+//    loop has no workgroup barrier.  The q-tiles of one split are launched
+//    onto one XCD (block id modulo 8) so that their common KV stream is
+//    fetched from HBM once and served from that XCD's L2.
+//  * Tiles move by direct global->LDS loads (no staging registers), K two
+//    tiles ahead and V one tile ahead, with explicit in-order vmcnt waits.
+//  * Scores are formed transposed, S^T = K Q^T (K rows are the A operand,
+//    16-byte LDS reads), so the probability tile comes out of the accumulator
+//    already in the B-operand order of O^T = V^T P^T; V^T comes from LDS with
+//    the transposing ds_read_b64_tr_b16.  P is never shuffled.
+//  * Software pipeline per wave: the scores of tile j+1 run on the matrix
+//    core while the VALU does the softmax of tile j.
 //  * Online softmax in log2 units; the running maximum only moves when a tile
 //    exceeds it by more than 2^8, so the O rescale is almost never paid.
-//  * Staged keys are rotated to P + depth(u) in registers (binary64 phase
-//    angles kept as fp32 cos/sin in LDS), written to cache rows P + u, and
+//  * Staged keys are rotated to P + depth(u) in LDS (binary64 phase angles
+//    kept as fp32 cos/sin), written to cache rows P + u by q-tile 0, and
 //    masked per lane with the packed ancestor bitmask.
 //  * The four wavefronts' (m, l, O) are merged through LDS; splits are merged
 //    by the last workgroup to finish (atomic arrival counter in the workspace,
@@ -101,24 +106,38 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// the values of lanes i and i ^ 32, in some order, for a cross-half max or sum
+__device__ __forceinline__ void halves(float v, float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
 // 32-bit LDS address of a __shared__ pointer, made wave-uniform
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(
       uint32_t(size_t((__attribute__((address_space(3))) const void*)(p))));
 }
 
-// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at lds + 16 l.
-// Issued as inline assembly so that the compiler does not pair it with a full
-// vmcnt(0) drain before every LDS read; the tile pipeline waits with explicit,
-// in-order vmcnt counts instead (an extra load issued later only lengthens a wait).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// Direct global -> LDS load of 16 bytes per lane from base + voff (base wave-uniform):
+// lane l's bytes land at lds + 16 l.  Issued as inline assembly so that the compiler
+// does not pair it with a full vmcnt(0) drain before every LDS read; the tile pipeline
+// waits with explicit, in-order vmcnt counts instead (a load issued later only
+// lengthens a wait).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds), "v"(g)
+               : "s"(lds), "v"(voff), "s"(base)
                : "memory", "m0");
 }
-__device__ __forceinline__ void wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm(int outstanding) {
+  if (outstanding >= 16)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (outstanding >= 8)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   const AttnArgs& a = p.a;
@@ -147,10 +166,77 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   const int N = a.N;
 
   __shared__ float2 s_cs[kTableDepth][kD / 2];
-  // two tile buffers per wave (K 8 KiB + V 8 KiB each); the final merge reuses them
-  __shared__ __attribute__((aligned(16))) unsigned char s_tile0[kWaves][16384];
-  __shared__ __attribute__((aligned(16))) unsigned char s_tile1[kWaves][16384];
+  // per wave: K and V double buffers of one 32 x 128 tile each; the final merge reuses them
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][kWaves][8192];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[2][kWaves][8192];
   __shared__ int s_int;
+
+  // ---- key range: split `split` of the committed prefix, plus the staged rows in the last split
+  const int per = ((P + p.splits - 1) / p.splits + kTile - 1) / kTile * kTile;
+  const int k_lo = min(P, split * per), k_hi = min(P, k_lo + per);
+  const int n_pre = (k_hi - k_lo + kTile - 1) / kTile;
+  const int n_stg = (split == p.splits - 1) ? (N + kTile - 1) / kTile : 0;
+  const int n_tiles = n_pre + n_stg;
+  // this wave's tiles are wave, wave + 4, wave + 8, ...
+  const int J = wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+  auto tile_of = [&](int j) __attribute__((always_inline)) { return wave + kWaves * j; };
+
+  const int64_t head = (int64_t(b) * a.Hkv + kvh) * a.S_max * kD;
+  const bf16* kc = static_cast<const bf16*>(a.k_cache) + head;
+  const bf16* vc = static_cast<const bf16*>(a.v_cache) + head;
+  bf16* kc_w = static_cast<bf16*>(a.k_cache) + head;
+  bf16* vc_w = static_cast<bf16*>(a.v_cache) + head;
+  const bf16* kn = static_cast<const bf16*>(a.k_new);
+  const bf16* vn = static_cast<const bf16*>(a.v_new);
+  auto kbuf = [&](int j) __attribute__((always_inline)) -> unsigned char* { return s_k[j & 1][wave]; };
+  auto vbuf = [&](int j) __attribute__((always_inline)) -> unsigned char* { return s_v[j & 1][wave]; };
+
+  // One tile's K or V rows into a buffer by direct global->LDS loads: instruction i moves
+  // rows 4 i .. 4 i + 3 (1 KiB, lane l -> bytes 16 l); lane l fetches logical chunk
+  // (l % 16) ^ (row % 16) so that the buffer holds the layout swz() reads back.  For a
+  // full prefix tile the byte offsets of rows 0..15 are fixed per lane (rows 16..31 use
+  // the same offsets from a base 16 rows further on).
+  const int n_full = (k_hi - k_lo) / kTile;
+  uint32_t poff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rt = 4 * i + (lane >> 4);
+    poff[i] = uint32_t(rt * 256 + (((lane & 15) ^ rt) << 4));
+  }
+  auto issue = [&](int t, bool is_v, unsigned char* buf) __attribute__((always_inline)) {
+    const uint32_t lds = lds_addr(buf);
+    if (t < n_full) {
+      const bf16* base = (is_v ? vc : kc) + int64_t(k_lo + t * kTile) * kD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dma16(base, poff[i], lds + 1024 * i);
+        dma16(base + 16 * kD, poff[i], lds + 1024 * (i + 4));
+      }
+    } else if (t < n_pre) {  // the partial prefix tile: rows past the split repeat row 0
+      const int k0 = k_lo + t * kTile;
+      const bf16* base = (is_v ? vc : kc) + int64_t(k0) * kD;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rt = 4 * i + (lane >> 4);
+        const int r = k0 + rt < k_hi ? rt : 0;
+        dma16(base, uint32_t(r * 256 + (((lane & 15) ^ (rt & 15)) << 4)), lds + 1024 * i);
+      }
+    } else {  // staged rows come from k_new / v_new; rows past the tree repeat row 0
+      const int v0 = (t - n_pre) * kTile;
+      const bf16* base = (is_v ? vn : kn) + (int64_t(b) * N * a.Hkv + kvh) * kD;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rt = 4 * i + (lane >> 4);
+        const int u = v0 + rt < N ? v0 + rt : 0;
+        dma16(base, uint32_t((u * a.Hkv * kD + 8 * ((lane & 15) ^ (rt & 15))) * 2), lds + 1024 * i);
+      }
+    }
+  };
+
+  // start the first tiles before the latency-bound set-up below
+  if (J > 0) issue(tile_of(0), false, kbuf(0));
+  if (J > 1) issue(tile_of(1), false, kbuf(1));
+  if (J > 0) issue(tile_of(0), true, vbuf(0));
 
   // ---- RoPE phases (cos, sin) of positions P + d for every depth d of the tree
   if (tid == 0) s_int = 0;
@@ -161,6 +247,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   __syncthreads();
   dmax = s_int;
   if (dmax >= kTableDepth) {  // uniform: every block sees the same tree
+    wait_vm(0);               // no load may still target LDS when the block exits
     if (blockIdx.x == 0 && tid == 0) raise_status(a.status, MEDUSA_EUNSUPPORTED);
     return;
   }
@@ -185,81 +272,29 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
     const int h = kvh * p.group + (live ? r % p.group : 0);
     qnode[c] = min(r / p.group, N - 1);
     const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t(b) * N + u) * a.Hq + h) * kD;
-    float x[8][8];
+    uint4 raw[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint4 raw = live ? *reinterpret_cast<const uint4*>(qr + 16 * s + 8 * half)
-                             : make_uint4(0, 0, 0, 0);
-      const bf16x8 v = __builtin_bit_cast(bf16x8, raw);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[s][e] = float(v[e]);
-    }
+    for (int s = 0; s < 8; ++s)
+      raw[s] = live ? *reinterpret_cast<const uint4*>(qr + 16 * s + 8 * half) : make_uint4(0, 0, 0, 0);
     const int dep = a.depth[u];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      const bf16x8 lo = __builtin_bit_cast(bf16x8, raw[s]);
+      const bf16x8 hi = __builtin_bit_cast(bf16x8, raw[s + 4]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float2 cs = s_cs[dep][16 * s + 8 * half + e];
-        const float x1 = x[s][e], x2 = x[s + 4][e];
-        x[s][e] = x1 * cs.x - x2 * cs.y;
-        x[s + 4][e] = x2 * cs.x + x1 * cs.y;
+        const float x1 = float(lo[e]), x2 = float(hi[e]);
+        qop[c][s][e] = static_cast<bf16>((x1 * cs.x - x2 * cs.y) * qscale);
+        qop[c][s + 4][e] = static_cast<bf16>((x2 * cs.x + x1 * cs.y) * qscale);
       }
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qop[c][s][e] = static_cast<bf16>(x[s][e] * qscale);
     }
   }
 
-  // ---- key range: split `split` of the committed prefix, plus the staged rows in the last split
-  const int per = ((P + p.splits - 1) / p.splits + kTile - 1) / kTile * kTile;
-  const int k_lo = min(P, split * per), k_hi = min(P, k_lo + per);
-  const int n_pre = (k_hi - k_lo + kTile - 1) / kTile;
-  const int n_stg = (split == p.splits - 1) ? (N + kTile - 1) / kTile : 0;
-  const int n_tiles = n_pre + n_stg;
-  const int steps = (n_tiles + kWaves - 1) / kWaves;
-
-  const int64_t head = (int64_t(b) * a.Hkv + kvh) * a.S_max * kD;
-  const bf16* kc = static_cast<const bf16*>(a.k_cache) + head;
-  const bf16* vc = static_cast<const bf16*>(a.v_cache) + head;
-  bf16* kc_w = static_cast<bf16*>(a.k_cache) + head;
-  bf16* vc_w = static_cast<bf16*>(a.v_cache) + head;
-  const bf16* kn = static_cast<const bf16*>(a.k_new);
-  const bf16* vn = static_cast<const bf16*>(a.v_new);
-
-  // Tile t lands in one of this wave's LDS buffers by direct global->LDS loads: instruction
-  // i moves rows 4 i .. 4 i + 3 (1 KiB, lane l -> bytes 16 l); lane l fetches logical chunk
-  // (l % 16) ^ (row % 16) so that the buffer holds the swizzled layout swz() reads.
-  auto issue_tile = [&](int t, unsigned char* buf) -> bool {
-    if (t >= n_tiles) return false;
-    const uint32_t base = lds_addr(buf);
-    const bool staged = t >= n_pre;
-    const int k0 = staged ? (t - n_pre) * kTile : k_lo + t * kTile;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rt = 4 * i + (lane >> 4);
-      const int c = (lane & 15) ^ (rt & 15);
-      const bf16 *ks, *vs;
-      if (staged) {
-        const int u = k0 + rt < N ? k0 + rt : 0;
-        const int64_t src = ((int64_t(b) * N + u) * a.Hkv + kvh) * kD;
-        ks = kn + src;
-        vs = vn + src;
-      } else {
-        const int row = k0 + rt < k_hi ? k0 + rt : k0;
-        ks = kc + int64_t(row) * kD;
-        vs = vc + int64_t(row) * kD;
-      }
-      dma16(ks + 8 * c, base + 1024 * i);
-      dma16(vs + 8 * c, base + 8192 + 1024 * i);
-    }
-    return true;
-  };
-  // Staged rows: rotate K in place to P + depth(u); q-tile 0 also stores K~ and V to cache
-  // rows P + u.  In each row every lane reads its chunk and the partner chunk (dims -+ 64)
+  // Staged rows: rotate K in place to P + depth(u); q-tile 0 also stores K~ to cache rows
+  // P + u.  In each row every lane reads its chunk and the partner chunk (dims -+ 64)
   // before any lane of the wave writes.
-  auto rotate_staged = [&](int t, unsigned char* buf) {
+  auto rotate_staged = [&](int t, unsigned char* buf) __attribute__((always_inline)) {
     const int v0 = (t - n_pre) * kTile;
     const int c = lane & 15;
     for (int i = 0; i < 8; ++i) {
@@ -267,9 +302,8 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
       const int uu = v0 + rt;
       const int u = uu < N ? uu : 0;
       uint4* kx = reinterpret_cast<uint4*>(buf + swz(rt, c));
-      const uint4 xr = *kx;
-      const uint4 yr = *reinterpret_cast<const uint4*>(buf + swz(rt, c ^ 8));
-      const bf16x8 xv = __builtin_bit_cast(bf16x8, xr), yv = __builtin_bit_cast(bf16x8, yr);
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, *kx);
+      const bf16x8 yv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(buf + swz(rt, c ^ 8)));
       const int dep = a.depth[u];
       bf16x8 rot;
 #pragma unroll
@@ -281,13 +315,45 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
       const uint4 rr = __builtin_bit_cast(uint4, rot);
       __builtin_amdgcn_wave_barrier();
       *kx = rr;
-      if (qt == 0 && uu < N) {
-        const int64_t dst = (int64_t(P) + uu) * kD + c * 8;
-        *reinterpret_cast<uint4*>(kc_w + dst) = rr;
-        *reinterpret_cast<uint4*>(vc_w + dst) = *reinterpret_cast<const uint4*>(buf + 8192 + swz(rt, c));
-      }
+      if (qt == 0 && uu < N)
+        *reinterpret_cast<uint4*>(kc_w + (int64_t(P) + uu) * kD + c * 8) = rr;
       __builtin_amdgcn_wave_barrier();
     }
+  };
+  // Staged rows: q-tile 0 copies V to cache rows P + u
+  auto store_staged_v = [&](int t, const unsigned char* buf) __attribute__((always_inline)) {
+    const int v0 = (t - n_pre) * kTile;
+    const int c = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rt = 4 * i + (lane >> 4);
+      if (v0 + rt < N)
+        *reinterpret_cast<uint4*>(vc_w + (int64_t(P) + v0 + rt) * kD + c * 8) =
+            *reinterpret_cast<const uint4*>(buf + swz(rt, c));
+    }
+  };
+  // S^T = K Q^T for one tile: 32 keys x 64 query columns
+  auto qk = [&](const unsigned char* kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[c][e] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + swz(l32, 2 * st + half)));
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[0][st], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[1][st], s[1], 0, 0, 0);
+    }
+  };
+  // visibility bits of a tile's 32 keys for query column block c (bit m = key m of the tile)
+  auto tile_bits = [&](int t, int c) __attribute__((always_inline)) -> uint32_t {
+    if (t < n_pre) {
+      const int nvalid = k_hi - (k_lo + t * kTile);
+      return nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+    }
+    const int v0 = (t - n_pre) * kTile;
+    const uint64_t word = a.mask[int64_t(qnode[c]) * a.mask_words + (v0 >> 6)];
+    return uint32_t(word >> (v0 & 63));
   };
 
   f32x16 oacc[4][2];
@@ -299,61 +365,56 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
       for (int e = 0; e < 16; ++e) oacc[db][c][e] = 0.f;
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-  // One pipeline step: start the wave's next tile into `nxt`, then compute on `cur`.
-  auto step = [&](int st, unsigned char* cur, unsigned char* nxt) {
-    const int t = st * kWaves + wave;
-    const bool ahead = issue_tile(t + kWaves, nxt);
-    if (t >= n_tiles) return;
-    if (ahead) wait_vm16();  // this tile's 16 loads are done; the next tile's 16 stay in flight
-    else wait_vm0();
-    if (t >= n_pre) rotate_staged(t, cur);
-    const unsigned char* kb = cur;
-    const unsigned char* vb = cur + 8192;
+  // per-lane LDS offsets of the V^T operand reads: 32-dim block db, key group h of the
+  // 16-key step; the step t2 adds 16 rows (4096 bytes) to both
+  const int gq = lane >> 4, gi = lane & 15;
+  int voff[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int dim = db * 32 + 16 * (gq & 1) + 4 * (gi & 3);
+    const int key0 = 4 * (gq >> 1) + (gi >> 2);
+    voff[db][0] = swz(key0, dim >> 3) + ((dim & 4) << 1);
+    voff[db][1] = swz(key0 + 8, dim >> 3) + ((dim & 4) << 1);
+  }
 
-    // S^T = K Q^T: keys of the tile (rows) x 64 query columns, in two 32-column blocks
-    f32x16 sacc[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[c][e] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + swz(l32, 2 * s + half)));
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[0][s], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[1][s], sacc[1], 0, 0, 0);
+  // The wave's tiles in order: full prefix tiles first (the pipelined main loop), then at
+  // most one partial prefix tile and the staged tiles (the tail, which masks and rotates).
+  const int Jf = wave < n_full ? (n_full - wave + kWaves - 1) / kWaves : 0;
+
+  // start tile j+2's K and tile j+1's V; returns how many loads were issued
+  auto prefetch = [&](int j) __attribute__((always_inline)) -> int {
+    int n = 0;
+    if (j + 2 < J) {
+      issue(tile_of(j + 2), false, kbuf(j + 2));
+      n += 8;
     }
-
-    // visibility of the 16 keys this lane holds: key 8 (e / 4) + 4 half + e % 4
+    if (j + 1 < J) {
+      issue(tile_of(j + 1), true, vbuf(j + 1));
+      n += 8;
+    }
+    return n;
+  };
+  // running-max update of one tile's scores; rescales O and l in the rare case it moves
+  auto update_max = [&](f32x16 (&sc)[2], float (&m_use)[2]) __attribute__((always_inline)) {
+    bool grow_any = false;
+    bool grow[2];
+    float tmax[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      uint32_t bits;
-      if (t < n_pre) {
-        const int nvalid = k_hi - (k_lo + t * kTile);
-        bits = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
-      } else {
-        const int v0 = (t - n_pre) * kTile;
-        const uint64_t word = a.mask[int64_t(qnode[c]) * a.mask_words + (v0 >> 6)];
-        bits = uint32_t(word >> (v0 & 63));
-      }
+      float x = fmaxf(fmaxf(sc[c][0], sc[c][1]), fmaxf(sc[c][2], sc[c][3]));
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = 8 * (e >> 2) + 4 * half + (e & 3);
-        if (!((bits >> m) & 1u)) sacc[c][e] = -INFINITY;
-      }
+      for (int e = 4; e < 16; e += 2) x = fmaxf(x, fmaxf(sc[c][e], sc[c][e + 1]));
+      float y0, y1;
+      halves(x, y0, y1);
+      tmax[c] = fmaxf(y0, y1);
+      grow[c] = tmax[c] > m_run[c] + kRescaleSlack;
+      grow_any = grow_any || grow[c];
     }
-
-    // online softmax (log2 units) per query column
-    bf16x8 pop[2][2];
+    if (__ballot(grow_any)) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float tmax = sacc[c][0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, sacc[c][e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const bool grow = tmax > m_run[c] + kRescaleSlack;
-      if (__ballot(grow)) {
-        const float m_new = grow ? tmax : m_run[c];
-        const float corr = grow ? exp2_fast(m_run[c] - m_new) : 1.0f;
+      for (int c = 0; c < 2; ++c) {
+        const float m_new = grow[c] ? tmax[c] : m_run[c];
+        const float corr = grow[c] ? exp2_fast(m_run[c] - m_new) : 1.0f;
         l_run[c] *= corr;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -361,36 +422,37 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
           for (int e = 0; e < 16; ++e) oacc[db][c][e] *= corr;
         m_run[c] = m_new;
       }
-      const float msafe = m_run[c] == -INFINITY ? 0.f : m_run[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) m_use[c] = m_run[c] == -INFINITY ? 0.f : m_run[c];
+  };
+  // probabilities of one tile (in place), their row sums, and the bf16 B operands of P^T
+  auto softmax = [&](f32x16 (&sc)[2], const float (&m_use)[2], bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pe = exp2_fast(sacc[c][e] - msafe);
-        sacc[c][e] = pe;
+        const float pe = exp2_fast(sc[c][e] - m_use[c]);
+        sc[c][e] = pe;
         psum += pe;
       }
       l_run[c] += psum;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pop[c][t2][e] = static_cast<bf16>(sacc[c][8 * t2 + e]);
+        for (int e = 0; e < 8; ++e) pop[c][t2][e] = static_cast<bf16>(sc[c][8 * t2 + e]);
     }
-
-    // O^T += V^T P^T: V^T operand for (32-dim block db, 16-key step t2) via transposing reads;
-    // k index 8 h + e of the step pairs with key 16 t2 + 8 (e / 4) + 4 h + e % 4, which is
-    // exactly the order in which the score accumulator holds P
-    const int gq = lane >> 4, gi = lane & 15;
+  };
+  // O^T += V^T P^T: k index 8 h + e of a 16-key step pairs with key 16 t2 + 8 (e / 4) +
+  // 4 h + e % 4, exactly the order in which the score accumulator holds P
+  auto pv = [&](const unsigned char* vb, const bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int dim = db * 32 + 16 * (gq & 1) + 4 * (gi & 3);
-      const int doff = (dim & 4) << 1;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const int key0 = 16 * t2 + 4 * (gq >> 1) + (gi >> 2);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vb + swz(key0, dim >> 3) + doff));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vb + swz(key0 + 8, dim >> 3) + doff));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][0] + 4096 * t2));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][1] + 4096 * t2));
         const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[0][t2], oacc[db][0], 0, 0, 0);
         oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[1][t2], oacc[db][1], 0, 0, 0);
@@ -398,22 +460,65 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
     }
   };
 
-  // double-buffered stream over this wave's tiles; the two buffers are distinct LDS objects
-  unsigned char* buf0 = s_tile0[wave];
-  unsigned char* buf1 = s_tile1[wave];
-  issue_tile(wave, buf0);
-  for (int st = 0; st < steps; st += 2) {
-    step(st, buf0, buf1);
-    if (st + 1 < steps) step(st + 1, buf1, buf0);
+  f32x16 s_a[2], s_b[2];
+  if (J > 0) wait_vm(0);
+  if (Jf > 0) qk(kbuf(0), s_a);
+
+  // main loop over full prefix tiles: the scores of tile j+1 run on the matrix core while
+  // the VALU turns tile j into probabilities
+  auto iter = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) __attribute__((always_inline)) {
+    wait_vm(prefetch(j));  // K of tile j+1 and V of tile j have landed
+    float m_use[2];
+    update_max(s_cur, m_use);
+    if (j + 1 < Jf) qk(kbuf(j + 1), s_nxt);
+    bf16x8 pop[2][2];
+    softmax(s_cur, m_use, pop);
+    pv(vbuf(j), pop);
+  };
+  for (int j = 0; j < Jf; j += 2) {
+    iter(j, s_a, s_b);
+    if (j + 1 < Jf) iter(j + 1, s_b, s_a);
+  }
+
+  // tail: partial prefix tile and staged tiles, one at a time.  Tile j's scores are formed
+  // here, so K of tile j+2 (same buffer as tile j) is only started once they are.
+  for (int j = Jf; j < J; ++j) {
+    const int t = tile_of(j);
+    wait_vm(0);  // K and V of tile j have landed
+    if (j + 1 < J) issue(tile_of(j + 1), true, vbuf(j + 1));
+    if (t >= n_pre) {
+      if (qt == 0) store_staged_v(t, vbuf(j));
+      rotate_staged(t, kbuf(j));
+    }
+    qk(kbuf(j), s_a);
+    if (j + 2 < J) issue(tile_of(j + 2), false, kbuf(j + 2));
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t bits = tile_bits(t, c);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = 8 * (e >> 2) + 4 * half + (e & 3);
+        if (!((bits >> m) & 1u)) s_a[c][e] = -INFINITY;
+      }
+    }
+    float m_use[2];
+    update_max(s_a, m_use);
+    bf16x8 pop[2][2];
+    softmax(s_a, m_use, pop);
+    pv(vbuf(j), pop);
   }
 
   // ---- merge the four wavefronts through LDS (two passes of 64 dims)
   float lsum[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) lsum[c] = l_run[c] + __shfl_xor(l_run[c], 32, 64);
+  for (int c = 0; c < 2; ++c) {
+    float y0, y1;
+    halves(l_run[c], y0, y1);
+    lsum[c] = y0 + y1;
+  }
   __syncthreads();
-  float* obuf = reinterpret_cast<float*>(&s_tile0[0][0]);    // [wave][64 q][64 dims]
-  float2* mlb = reinterpret_cast<float2*>(&s_tile1[0][0]);   // [wave][64 q]
+  float* obuf = reinterpret_cast<float*>(&s_k[0][0][0]);    // [wave][64 q][64 dims]
+  float2* mlb = reinterpret_cast<float2*>(&s_v[0][0][0]);   // [wave][64 q]
   if (half == 0) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) mlb[wave * 64 + c * 32 + l32] = make_float2(m_run[c], lsum[c]);
@@ -422,7 +527,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   if (p.splits > 1)
     part = reinterpret_cast<Partial*>(static_cast<unsigned char*>(a.workspace) + p.partial_offset) +
            (int64_t(unit) * p.qtiles + qt) * p.splits + split;
-  auto store_out = [&](int q, int dim0, float4 v) {
+  auto store_out = [&](int q, int dim0, float4 v) __attribute__((always_inline)) {
     const int r = qt * kRowsWG + q;
     if (r >= p.rows) return;
     const int u = r / p.group, h = kvh * p.group + r % p.group;
