@@ -7,33 +7,36 @@
 // of w or w itself) -- the same contract as the wavefront-per-row path.
 //
 // Mapping to CDNA4:
-//  * One (sequence b, kv head g) pair owns a query block of N * (Hq/Hkv) rows:
-//    every tree node times every query head of the GQA group.  That block
-//    against a key tile is a dense contraction, so both products run on
-//    v_mfma_f32_32x32x16_bf16.
-//  * A workgroup takes 64 query rows (a q-tile) and one contiguous split of
-//    the committed prefix; the last split also takes the staged rows.  Its
-//    four wavefronts hold the same 64 rotated, pre-scaled query rows in
-//    registers and each streams its own interleaved 32-key tiles, so the main
-//    loop has no workgroup barrier.  The q-tiles of one split are launched
-//    onto one XCD (block id modulo 8) so that their common KV stream is
-//    fetched from HBM once and served from that XCD's L2.
-//  * Tiles move by direct global->LDS loads (no staging registers), K two
-//    tiles ahead and V one tile ahead, with explicit in-order vmcnt waits.
+//  * One (sequence b, kv head g) pair -- a unit -- owns a query block of
+//    N * (Hq/Hkv) rows: every tree node times every query head of the GQA group.
+//    That block against a key tile is a dense contraction, so both products run
+//    on v_mfma_f32_32x32x16_bf16.  With 256 rows per unit each key byte feeds
+//    about as many flops as the matrix cores retire per HBM byte, so the kernel
+//    is balanced between HBM and MFMA and must overlap the two.
+//  * A workgroup takes up to 256 query rows of one unit (four wavefronts of 64
+//    rows) and one contiguous split of the unit's key tiles: the committed prefix
+//    followed by the staged rows.  Every key tile is fetched from HBM once, into
+//    LDS, and read there by all four wavefronts.  Query blocks of 128 rows or
+//    fewer use two key phases instead: wavefront pairs take alternate tiles.
+//  * The LDS holds a ring of eight 32-key tiles (K and V, 128 KiB) filled by
+//    direct global->LDS loads up to seven tiles ahead, so that about 100 KiB per
+//    CU is in flight, which is what HBM latency times bandwidth asks for.  Each
+//    wavefront loads its eight rows of every tile; one workgroup barrier per
+//    tile publishes the tile and frees the slot of the tile before.
 //  * Scores are formed transposed, S^T = K Q^T (K rows are the A operand,
 //    16-byte LDS reads), so the probability tile comes out of the accumulator
 //    already in the B-operand order of O^T = V^T P^T; V^T comes from LDS with
 //    the transposing ds_read_b64_tr_b16.  P is never shuffled.
-//  * Software pipeline per wave: the scores of tile j+1 run on the matrix
+//  * Software pipeline per wavefront: the scores of tile j+1 run on the matrix
 //    core while the VALU does the softmax of tile j.
 //  * Online softmax in log2 units; the running maximum only moves when a tile
 //    exceeds it by more than 2^8, so the O rescale is almost never paid.
-//  * Staged keys are rotated to P + depth(u) in LDS (binary64 phase angles
-//    kept as fp32 cos/sin), written to cache rows P + u by q-tile 0, and
-//    masked per lane with the packed ancestor bitmask.
-//  * The four wavefronts' (m, l, O) are merged through LDS; splits are merged
-//    by the last workgroup to finish (atomic arrival counter in the workspace,
-//    reset by that workgroup), so one launch does the whole call.
+//  * Staged keys are rotated to P + depth(u) in LDS by the wavefront that
+//    loaded them (binary64 phase angles kept as fp32 cos/sin), written to cache
+//    rows P + u by query block 0, and masked per lane with the ancestor bitmask.
+//  * Splits of one query block are merged by a second, small kernel from
+//    (m, l, O) partials in the workspace; with a single split the first kernel
+//    writes the output itself.
 
 #include <cmath>
 
@@ -43,10 +46,13 @@ namespace medusa {
 namespace {
 
 constexpr int kD = 128;          // head dimension
-constexpr int kRowsWG = 64;      // query rows per workgroup
 constexpr int kTile = 32;        // keys per tile
 constexpr int kWaves = 4;
+constexpr int kRowsWave = 64;    // query rows per wavefront
+constexpr int kRing = 8;         // tile buffers in LDS
+constexpr int kTileBytes = 2 * kTile * kD * 2;  // K then V of one tile
 constexpr int kTableDepth = 32;  // RoPE phases kept in LDS; deeper trees are rejected
+constexpr int kDepthLds = 8192;  // node depths cached in LDS (bytes); later nodes read HBM
 constexpr int kTargetWGs = 256;  // one workgroup per compute unit
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
@@ -59,25 +65,29 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct MfmaArgs {
   AttnArgs a;
-  int32_t group;           // Hq / Hkv
-  int32_t rows;            // N * group query rows per (sequence, kv head)
-  int32_t qtiles;          // ceil(rows / 64)
-  int32_t splits;          // workgroups sharing one q-tile's keys
-  int32_t xcd_map;         // keep the q-tiles of one (unit, split) on one XCD
-  int32_t partial_offset;  // byte offset of the split partials in the workspace
-  double theta[kD / 2];    // RoPE inverse frequencies base^(-2i/d)
+  int32_t group;     // Hq / Hkv
+  int32_t rows;      // N * group query rows per unit
+  int32_t n_kp;      // key phases: 1 (four wavefronts share every tile) or 2
+  int32_t qrows;     // query rows per workgroup: 64 * 4 / n_kp
+  int32_t qblocks;   // ceil(rows / qrows)
+  int32_t splits;    // workgroups sharing one query block's keys
+  int32_t xcd_map;   // keep the query blocks of one (unit, split) on one XCD
+  int64_t o_offset;  // byte offset of the partial O in the workspace
+  double theta[kD / 2];  // RoPE inverse frequencies base^(-2i/d)
 };
 
-struct Partial {
-  float m[kRowsWG];
-  float l[kRowsWG];
-  float o[kRowsWG][kD];
+struct MergeArgs {
+  const float2* ml;  // [units][qblocks][splits][qrows] (m, l)
+  const float* o;    // [units][qblocks][splits][qrows][D]
+  void* out;
+  const int32_t* status;
+  int32_t Hq, Hkv, N, group, rows, qrows, qblocks, splits;
 };
 
 struct Plan {
-  int32_t units, group, rows, qtiles, splits;
+  int32_t units, group, rows, n_kp, qrows, qblocks, splits;
   bool xcd_map;
-  size_t partial_offset, bytes;
+  size_t o_offset, bytes;
 };
 
 Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
@@ -85,20 +95,24 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
   p.units = B * Hkv;
   p.group = Hq / Hkv;
   p.rows = N * p.group;
-  p.qtiles = (p.rows + kRowsWG - 1) / kRowsWG;
-  const int32_t wgs = p.units * p.qtiles;
+  p.n_kp = p.rows > 2 * kRowsWave ? 1 : 2;
+  p.qrows = kRowsWave * kWaves / p.n_kp;
+  p.qblocks = (p.rows + p.qrows - 1) / p.qrows;
+  const int32_t wgs = p.units * p.qblocks;
   int32_t splits = (kTargetWGs + wgs / 2) / wgs;
-  const int32_t max_splits = (S_max - N) / 256;  // at least ~256 prefix keys per split
-  splits = splits < max_splits ? splits : max_splits;
+  // at least four stages of tiles per split
+  const int64_t tiles = (int64_t(S_max) - N + kTile - 1) / kTile + (N + kTile - 1) / kTile;
+  const int64_t max_splits = tiles / (4 * p.n_kp);
+  splits = splits < max_splits ? splits : int32_t(max_splits);
   p.splits = splits < 1 ? 1 : splits;
-  p.xcd_map = (int64_t(p.units) * p.splits) % 8 == 0;
-  p.partial_offset = (size_t(p.units) * p.qtiles * sizeof(int32_t) + 255) / 256 * 256;
-  p.bytes = p.partial_offset +
-            (p.splits > 1 ? size_t(p.units) * p.qtiles * p.splits * sizeof(Partial) : 0);
+  p.xcd_map = p.qblocks > 1 && (int64_t(p.units) * p.splits) % 8 == 0;
+  const size_t slots = size_t(p.units) * p.qblocks * p.splits * p.qrows;
+  p.o_offset = (slots * sizeof(float2) + 255) / 256 * 256;
+  p.bytes = p.splits > 1 ? p.o_offset + slots * kD * sizeof(float) : 256;
   return p;
 }
 
-// byte offset of (row, 16-byte chunk) in a 32 x 256-byte tile; chunks are
+// byte offset of (row, 16-byte chunk) in a 32 x 256-byte matrix; chunks are
 // XOR-swizzled by row so that column reads spread over the LDS banks
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 256 + ((chunk ^ (row & 15)) << 4);
@@ -121,22 +135,33 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Direct global -> LDS load of 16 bytes per lane from base + voff (base wave-uniform):
 // lane l's bytes land at lds + 16 l.  Issued as inline assembly so that the compiler
-// does not pair it with a full vmcnt(0) drain before every LDS read; the tile pipeline
+// does not pair it with a full vmcnt(0) drain before every LDS read; the tile ring
 // waits with explicit, in-order vmcnt counts instead (a load issued later only
 // lengthens a wait).
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t addr = uint64_t(base);
+  // readfirstlane yields a signed int: widen through uint32_t so the low word is not sign-extended
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(addr)));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(addr >> 32)));
+  const uint64_t sbase = uint64_t(lo) | (uint64_t(hi) << 32);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds), "v"(voff), "s"(base)
+               : "s"(lds), "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
-__device__ __forceinline__ void wait_vm(int outstanding) {
-  if (outstanding >= 16)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (outstanding >= 8)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+// wait until at most n of this wavefront's vector memory operations are outstanding
+// (n rounded down to a multiple of 4, which only makes the wait stricter)
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n >= 24 ? 6 : n >> 2) {
+    case 6: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
 }
 
 __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
@@ -149,100 +174,120 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5, l32 = lane & 31;
+  const int n_kp = p.n_kp;
+  const int kp = wave % n_kp, rb = wave / n_kp;  // key phase, 64-row block
 
-  // ---- this workgroup's (sequence, kv head, split, q-tile)
-  int grp, qt;
+  // ---- this workgroup's (sequence, kv head, split, query block)
+  int grp, qb;
   if (p.xcd_map) {
     const int slot = blockIdx.x >> 3;
-    grp = int(blockIdx.x & 7) + 8 * (slot / p.qtiles);
-    qt = slot % p.qtiles;
+    grp = int(blockIdx.x & 7) + 8 * (slot / p.qblocks);
+    qb = slot % p.qblocks;
   } else {
-    grp = blockIdx.x / p.qtiles;
-    qt = blockIdx.x % p.qtiles;
+    grp = blockIdx.x / p.qblocks;
+    qb = blockIdx.x % p.qblocks;
   }
   const int unit = grp / p.splits, split = grp % p.splits;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
   const int P = a.prefix_len[b];
   const int N = a.N;
 
+  __shared__ __attribute__((aligned(16))) unsigned char s_ring[kRing][kTileBytes];
   __shared__ float2 s_cs[kTableDepth][kD / 2];
-  // per wave: K and V double buffers of one 32 x 128 tile each; the final merge reuses them
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][kWaves][8192];
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[2][kWaves][8192];
+  __shared__ unsigned char s_dep[kDepthLds];
   __shared__ int s_int;
 
-  // ---- key range: split `split` of the committed prefix, plus the staged rows in the last split
-  const int per = ((P + p.splits - 1) / p.splits + kTile - 1) / kTile * kTile;
-  const int k_lo = min(P, split * per), k_hi = min(P, k_lo + per);
-  const int n_pre = (k_hi - k_lo + kTile - 1) / kTile;
-  const int n_stg = (split == p.splits - 1) ? (N + kTile - 1) / kTile : 0;
-  const int n_tiles = n_pre + n_stg;
-  // this wave's tiles are wave, wave + 4, wave + 8, ...
-  const int J = wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
-  auto tile_of = [&](int j) __attribute__((always_inline)) { return wave + kWaves * j; };
+  // ---- key tiles of the unit: n_pre prefix tiles (the last one may be partial), then the
+  // staged tiles.  Stage i of this split holds tiles (s_lo + i) * n_kp + k, k < n_kp, in
+  // ring slot i % S.
+  const int n_pre = (P + kTile - 1) / kTile;
+  const int T = n_pre + (N + kTile - 1) / kTile;
+  const int n_stages = (T + n_kp - 1) / n_kp;
+  const int s_lo = int(int64_t(split) * n_stages / p.splits);
+  const int n_st = int(int64_t(split + 1) * n_stages / p.splits) - s_lo;
+  const int S = kRing / n_kp;  // 8 or 4 stages in the ring
+  auto tile_start = [&](int i) __attribute__((always_inline)) { return (s_lo + i) * n_kp; };
+  auto tile_end = [&](int i) __attribute__((always_inline)) { return min(T, (s_lo + i + 1) * n_kp); };
 
   const int64_t head = (int64_t(b) * a.Hkv + kvh) * a.S_max * kD;
   const bf16* kc = static_cast<const bf16*>(a.k_cache) + head;
   const bf16* vc = static_cast<const bf16*>(a.v_cache) + head;
   bf16* kc_w = static_cast<bf16*>(a.k_cache) + head;
   bf16* vc_w = static_cast<bf16*>(a.v_cache) + head;
-  const bf16* kn = static_cast<const bf16*>(a.k_new);
-  const bf16* vn = static_cast<const bf16*>(a.v_new);
-  auto kbuf = [&](int j) __attribute__((always_inline)) -> unsigned char* { return s_k[j & 1][wave]; };
-  auto vbuf = [&](int j) __attribute__((always_inline)) -> unsigned char* { return s_v[j & 1][wave]; };
+  const bf16* kn = static_cast<const bf16*>(a.k_new) + (int64_t(b) * N * a.Hkv + kvh) * kD;
+  const bf16* vn = static_cast<const bf16*>(a.v_new) + (int64_t(b) * N * a.Hkv + kvh) * kD;
+  // LDS buffer of stage i's k-th tile: K at +0, V at +8192
+  auto tbuf = [&](int i, int k) __attribute__((always_inline)) -> unsigned char* {
+    return s_ring[(i & (S - 1)) * n_kp + k];
+  };
 
-  // One tile's K or V rows into a buffer by direct global->LDS loads: instruction i moves
-  // rows 4 i .. 4 i + 3 (1 KiB, lane l -> bytes 16 l); lane l fetches logical chunk
-  // (l % 16) ^ (row % 16) so that the buffer holds the layout swz() reads back.  For a
-  // full prefix tile the byte offsets of rows 0..15 are fixed per lane (rows 16..31 use
-  // the same offsets from a base 16 rows further on).
-  const int n_full = (k_hi - k_lo) / kTile;
-  uint32_t poff[4];
+  // Rows 8 w .. 8 w + 7 of one tile's K and V by direct global->LDS loads (wavefront w,
+  // two instructions of four rows per matrix): lane l lands at byte 1024 i + 16 l of the
+  // matrix, i.e. row 4 i + l / 16, stored chunk l % 16, and fetches logical chunk
+  // (l % 16) ^ (row % 16), so that the buffer holds the layout swz() reads back.
+  uint32_t poff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rt = 4 * i + (lane >> 4);
-    poff[i] = uint32_t(rt * 256 + (((lane & 15) ^ rt) << 4));
+  for (int h = 0; h < 2; ++h) {
+    const int rt = 4 * (2 * wave + h) + (lane >> 4);
+    poff[h] = uint32_t(rt * 256 + (((lane & 15) ^ (rt & 15)) << 4));
   }
-  auto issue = [&](int t, bool is_v, unsigned char* buf) __attribute__((always_inline)) {
-    const uint32_t lds = lds_addr(buf);
-    if (t < n_full) {
-      const bf16* base = (is_v ? vc : kc) + int64_t(k_lo + t * kTile) * kD;
+  auto issue_tile = [&](int t, unsigned char* buf) __attribute__((always_inline)) {
+    const uint32_t lds = lds_addr(buf) + 2048 * wave;
+    if ((t + 1) * kTile <= P) {  // full prefix tile
+      const int64_t off = int64_t(t) * kTile * kD;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dma16(base, poff[i], lds + 1024 * i);
-        dma16(base + 16 * kD, poff[i], lds + 1024 * (i + 4));
+      for (int h = 0; h < 2; ++h) {
+        dma16(kc + off, poff[h], lds + 1024 * h);
+        dma16(vc + off, poff[h], lds + 8192 + 1024 * h);
       }
-    } else if (t < n_pre) {  // the partial prefix tile: rows past the split repeat row 0
-      const int k0 = k_lo + t * kTile;
-      const bf16* base = (is_v ? vc : kc) + int64_t(k0) * kD;
+    } else if (t < n_pre) {  // the partial prefix tile: rows past P repeat row 0
+      const int64_t off = int64_t(t) * kTile * kD;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int rt = 4 * i + (lane >> 4);
-        const int r = k0 + rt < k_hi ? rt : 0;
-        dma16(base, uint32_t(r * 256 + (((lane & 15) ^ (rt & 15)) << 4)), lds + 1024 * i);
+      for (int h = 0; h < 2; ++h) {
+        const int rt = 4 * (2 * wave + h) + (lane >> 4);
+        const int r = t * kTile + rt < P ? rt : 0;
+        const uint32_t o = uint32_t(r * 256 + (((lane & 15) ^ (rt & 15)) << 4));
+        dma16(kc + off, o, lds + 1024 * h);
+        dma16(vc + off, o, lds + 8192 + 1024 * h);
       }
-    } else {  // staged rows come from k_new / v_new; rows past the tree repeat row 0
+    } else {  // staged rows from k_new / v_new; rows past the tree repeat node 0
       const int v0 = (t - n_pre) * kTile;
-      const bf16* base = (is_v ? vn : kn) + (int64_t(b) * N * a.Hkv + kvh) * kD;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int rt = 4 * i + (lane >> 4);
+      for (int h = 0; h < 2; ++h) {
+        const int rt = 4 * (2 * wave + h) + (lane >> 4);
         const int u = v0 + rt < N ? v0 + rt : 0;
-        dma16(base, uint32_t((u * a.Hkv * kD + 8 * ((lane & 15) ^ (rt & 15))) * 2), lds + 1024 * i);
+        const uint32_t o = uint32_t((u * a.Hkv * kD + 8 * ((lane & 15) ^ (rt & 15))) * 2);
+        dma16(kn, o, lds + 1024 * h);
+        dma16(vn, o, lds + 8192 + 1024 * h);
       }
     }
   };
+  auto issue_stage = [&](int i) __attribute__((always_inline)) {
+    for (int k = 0; k < n_kp; ++k) {
+      const int t = tile_start(i) + k;
+      if (t < T) issue_tile(t, tbuf(i, k));
+    }
+  };
+  // wait until this wavefront's loads of stage i have landed, stages up to `last` having
+  // been issued (four loads per tile)
+  auto wait_stage = [&](int i, int last) __attribute__((always_inline)) {
+    wait_vm(last > i ? 4 * (tile_end(last) - tile_end(i)) : 0);
+  };
 
-  // start the first tiles before the latency-bound set-up below
-  if (J > 0) issue(tile_of(0), false, kbuf(0));
-  if (J > 1) issue(tile_of(1), false, kbuf(1));
-  if (J > 0) issue(tile_of(0), true, vbuf(0));
+  // fill the ring, all but one slot, before the latency-bound set-up below
+  const int first = min(S - 1, n_st);
+  for (int i = 0; i < first; ++i) issue_stage(i);
 
-  // ---- RoPE phases (cos, sin) of positions P + d for every depth d of the tree
+  // ---- node depths (LDS copy) and the RoPE phases (cos, sin) of positions P + d for
+  // every depth d of the tree
   if (tid == 0) s_int = 0;
   __syncthreads();
   int dmax = 0;
-  for (int i = tid; i < N; i += 256) dmax = max(dmax, a.depth[i]);
+  for (int i = tid; i < N; i += 256) {
+    const int d = a.depth[i];
+    dmax = max(dmax, d);
+    if (i < kDepthLds) s_dep[i] = static_cast<unsigned char>(d);
+  }
   atomicMax(&s_int, dmax);
   __syncthreads();
   dmax = s_int;
@@ -258,25 +303,29 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
     s_cs[d][j] = make_float2(float(cs), float(sn));
   }
   __syncthreads();
+  auto depth_of = [&](int u) __attribute__((always_inline)) -> int {
+    return u < kDepthLds ? int(s_dep[u]) : a.depth[u];
+  };
 
-  // ---- query rows of this q-tile: rotated, scaled to log2 units, bf16 B operands
+  // ---- this wavefront's 64 query rows: rotated, scaled to log2 units, bf16 B operands;
   // lane holds query column l32 of column block c, dims 16 s + 8 half + e (e < 8)
+  const int row0 = qb * p.qrows + rb * kRowsWave;
   const float qscale = kLog2e / sqrtf(float(kD));
   bf16x8 qop[2][8];
   int qnode[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const int r = qt * kRowsWG + c * 32 + l32;
+    const int r = row0 + c * 32 + l32;
     const bool live = r < p.rows;
     const int u = live ? r / p.group : 0;
     const int h = kvh * p.group + (live ? r % p.group : 0);
-    qnode[c] = min(r / p.group, N - 1);
+    qnode[c] = u;
     const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t(b) * N + u) * a.Hq + h) * kD;
     uint4 raw[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       raw[s] = live ? *reinterpret_cast<const uint4*>(qr + 16 * s + 8 * half) : make_uint4(0, 0, 0, 0);
-    const int dep = a.depth[u];
+    const int dep = depth_of(u);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 lo = __builtin_bit_cast(bf16x8, raw[s]);
@@ -291,47 +340,44 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
     }
   }
 
-  // Staged rows: rotate K in place to P + depth(u); q-tile 0 also stores K~ to cache rows
-  // P + u.  In each row every lane reads its chunk and the partner chunk (dims -+ 64)
-  // before any lane of the wave writes.
-  auto rotate_staged = [&](int t, unsigned char* buf) __attribute__((always_inline)) {
-    const int v0 = (t - n_pre) * kTile;
-    const int c = lane & 15;
-    for (int i = 0; i < 8; ++i) {
-      const int rt = 4 * i + (lane >> 4);
-      const int uu = v0 + rt;
-      const int u = uu < N ? uu : 0;
-      uint4* kx = reinterpret_cast<uint4*>(buf + swz(rt, c));
-      const bf16x8 xv = __builtin_bit_cast(bf16x8, *kx);
-      const bf16x8 yv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(buf + swz(rt, c ^ 8)));
-      const int dep = a.depth[u];
-      bf16x8 rot;
+  // Staged rows of one tile that this wavefront loaded (rows 8 w .. 8 w + 7): rotate K in
+  // place to P + depth(u); query block 0 also stores K~ and V to cache rows P + u.  Lane l
+  // takes row 8 w + l / 8 and the chunk pair (l % 8, l % 8 + 8), i.e. dims j and j + 64.
+  auto fix_staged = [&](int t, unsigned char* buf) __attribute__((always_inline)) {
+    const int rt = 8 * wave + (lane >> 3), c = lane & 7;
+    const int uu = (t - n_pre) * kTile + rt;
+    const int dep = depth_of(uu < N ? uu : 0);
+    uint4* px = reinterpret_cast<uint4*>(buf + swz(rt, c));
+    uint4* py = reinterpret_cast<uint4*>(buf + swz(rt, c + 8));
+    const bf16x8 xv = __builtin_bit_cast(bf16x8, *px);
+    const bf16x8 yv = __builtin_bit_cast(bf16x8, *py);
+    bf16x8 rx, ry;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 cs = s_cs[dep][8 * (c & 7) + e];
-        const float x = float(xv[e]), y = float(yv[e]);
-        rot[e] = static_cast<bf16>(c < 8 ? x * cs.x - y * cs.y : x * cs.x + y * cs.y);
-      }
-      const uint4 rr = __builtin_bit_cast(uint4, rot);
-      __builtin_amdgcn_wave_barrier();
-      *kx = rr;
-      if (qt == 0 && uu < N)
-        *reinterpret_cast<uint4*>(kc_w + (int64_t(P) + uu) * kD + c * 8) = rr;
-      __builtin_amdgcn_wave_barrier();
+    for (int e = 0; e < 8; ++e) {
+      const float2 cs = s_cs[dep][8 * c + e];
+      const float x = float(xv[e]), y = float(yv[e]);
+      rx[e] = static_cast<bf16>(x * cs.x - y * cs.y);
+      ry[e] = static_cast<bf16>(y * cs.x + x * cs.y);
+    }
+    *px = __builtin_bit_cast(uint4, rx);
+    *py = __builtin_bit_cast(uint4, ry);
+    if (qb == 0 && uu < N) {
+      bf16* kd = kc_w + (int64_t(P) + uu) * kD;
+      bf16* vd = vc_w + (int64_t(P) + uu) * kD;
+      *reinterpret_cast<uint4*>(kd + 8 * c) = __builtin_bit_cast(uint4, rx);
+      *reinterpret_cast<uint4*>(kd + 8 * c + 64) = __builtin_bit_cast(uint4, ry);
+      *reinterpret_cast<uint4*>(vd + 8 * c) = *reinterpret_cast<const uint4*>(buf + 8192 + swz(rt, c));
+      *reinterpret_cast<uint4*>(vd + 8 * c + 64) = *reinterpret_cast<const uint4*>(buf + 8192 + swz(rt, c + 8));
     }
   };
-  // Staged rows: q-tile 0 copies V to cache rows P + u
-  auto store_staged_v = [&](int t, const unsigned char* buf) __attribute__((always_inline)) {
-    const int v0 = (t - n_pre) * kTile;
-    const int c = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rt = 4 * i + (lane >> 4);
-      if (v0 + rt < N)
-        *reinterpret_cast<uint4*>(vc_w + (int64_t(P) + v0 + rt) * kD + c * 8) =
-            *reinterpret_cast<const uint4*>(buf + swz(rt, c));
+  // once stage i has landed: the staged tiles of the stage get their rows fixed
+  auto fix_stage = [&](int i) __attribute__((always_inline)) {
+    for (int k = 0; k < n_kp; ++k) {
+      const int t = tile_start(i) + k;
+      if (t >= n_pre && t < T) fix_staged(t, tbuf(i, k));
     }
   };
+
   // S^T = K Q^T for one tile: 32 keys x 64 query columns
   auto qk = [&](const unsigned char* kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -345,15 +391,20 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[1][st], s[1], 0, 0, 0);
     }
   };
-  // visibility bits of a tile's 32 keys for query column block c (bit m = key m of the tile)
-  auto tile_bits = [&](int t, int c) __attribute__((always_inline)) -> uint32_t {
+  // visibility bits of a tile's 32 keys for query column block c (bit m = key m of the
+  // tile); all ones for a full prefix tile
+  auto tile_bits = [&](int t, uint32_t (&bits)[2]) __attribute__((always_inline)) {
     if (t < n_pre) {
-      const int nvalid = k_hi - (k_lo + t * kTile);
-      return nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+      const int nvalid = P - t * kTile;
+      bits[0] = bits[1] = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+    } else {
+      const int v0 = (t - n_pre) * kTile;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint64_t word = a.mask[int64_t(qnode[c]) * a.mask_words + (v0 >> 6)];
+        bits[c] = uint32_t(word >> (v0 & 63));
+      }
     }
-    const int v0 = (t - n_pre) * kTile;
-    const uint64_t word = a.mask[int64_t(qnode[c]) * a.mask_words + (v0 >> 6)];
-    return uint32_t(word >> (v0 & 63));
   };
 
   f32x16 oacc[4][2];
@@ -373,27 +424,10 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   for (int db = 0; db < 4; ++db) {
     const int dim = db * 32 + 16 * (gq & 1) + 4 * (gi & 3);
     const int key0 = 4 * (gq >> 1) + (gi >> 2);
-    voff[db][0] = swz(key0, dim >> 3) + ((dim & 4) << 1);
-    voff[db][1] = swz(key0 + 8, dim >> 3) + ((dim & 4) << 1);
+    voff[db][0] = 8192 + swz(key0, dim >> 3) + ((dim & 4) << 1);
+    voff[db][1] = 8192 + swz(key0 + 8, dim >> 3) + ((dim & 4) << 1);
   }
 
-  // The wave's tiles in order: full prefix tiles first (the pipelined main loop), then at
-  // most one partial prefix tile and the staged tiles (the tail, which masks and rotates).
-  const int Jf = wave < n_full ? (n_full - wave + kWaves - 1) / kWaves : 0;
-
-  // start tile j+2's K and tile j+1's V; returns how many loads were issued
-  auto prefetch = [&](int j) __attribute__((always_inline)) -> int {
-    int n = 0;
-    if (j + 2 < J) {
-      issue(tile_of(j + 2), false, kbuf(j + 2));
-      n += 8;
-    }
-    if (j + 1 < J) {
-      issue(tile_of(j + 1), true, vbuf(j + 1));
-      n += 8;
-    }
-    return n;
-  };
   // running-max update of one tile's scores; rescales O and l in the rare case it moves
   auto update_max = [&](f32x16 (&sc)[2], float (&m_use)[2]) __attribute__((always_inline)) {
     bool grow_any = false;
@@ -446,13 +480,13 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   };
   // O^T += V^T P^T: k index 8 h + e of a 16-key step pairs with key 16 t2 + 8 (e / 4) +
   // 4 h + e % 4, exactly the order in which the score accumulator holds P
-  auto pv = [&](const unsigned char* vb, const bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
+  auto pv = [&](const unsigned char* tb, const bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][0] + 4096 * t2));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[db][1] + 4096 * t2));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb + voff[db][0] + 4096 * t2));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb + voff[db][1] + 4096 * t2));
         const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[0][t2], oacc[db][0], 0, 0, 0);
         oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[1][t2], oacc[db][1], 0, 0, 0);
@@ -460,55 +494,61 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
     }
   };
 
-  f32x16 s_a[2], s_b[2];
-  if (J > 0) wait_vm(0);
-  if (Jf > 0) qk(kbuf(0), s_a);
-
-  // main loop over full prefix tiles: the scores of tile j+1 run on the matrix core while
-  // the VALU turns tile j into probabilities
-  auto iter = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) __attribute__((always_inline)) {
-    wait_vm(prefetch(j));  // K of tile j+1 and V of tile j have landed
-    float m_use[2];
-    update_max(s_cur, m_use);
-    if (j + 1 < Jf) qk(kbuf(j + 1), s_nxt);
-    bf16x8 pop[2][2];
-    softmax(s_cur, m_use, pop);
-    pv(vbuf(j), pop);
+  // this wavefront's tile of stage i: visibility bits and scores
+  auto prep = [&](int i, f32x16 (&s)[2], uint32_t (&bits)[2]) __attribute__((always_inline)) {
+    const int t = tile_start(i) + kp;
+    if (t < T) {
+      tile_bits(t, bits);
+      qk(tbuf(i, kp), s);
+    }
   };
-  for (int j = 0; j < Jf; j += 2) {
-    iter(j, s_a, s_b);
-    if (j + 1 < Jf) iter(j + 1, s_b, s_a);
-  }
-
-  // tail: partial prefix tile and staged tiles, one at a time.  Tile j's scores are formed
-  // here, so K of tile j+2 (same buffer as tile j) is only started once they are.
-  for (int j = Jf; j < J; ++j) {
-    const int t = tile_of(j);
-    wait_vm(0);  // K and V of tile j have landed
-    if (j + 1 < J) issue(tile_of(j + 1), true, vbuf(j + 1));
-    if (t >= n_pre) {
-      if (qt == 0) store_staged_v(t, vbuf(j));
-      rotate_staged(t, kbuf(j));
-    }
-    qk(kbuf(j), s_a);
-    if (j + 2 < J) issue(tile_of(j + 2), false, kbuf(j + 2));
+  // masking, softmax and PV of this wavefront's tile of stage i
+  auto consume = [&](int i, f32x16 (&s)[2], const uint32_t (&bits)[2]) __attribute__((always_inline)) {
+    const int t = tile_start(i) + kp;
+    if (t >= T) return;
+    if (t >= n_pre - 1) {  // the last prefix tile or a staged tile
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint32_t bits = tile_bits(t, c);
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = 8 * (e >> 2) + 4 * half + (e & 3);
-        if (!((bits >> m) & 1u)) s_a[c][e] = -INFINITY;
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int m = 8 * (e >> 2) + 4 * half + (e & 3);
+          if (!((bits[c] >> m) & 1u)) s[c][e] = -INFINITY;
+        }
     }
     float m_use[2];
-    update_max(s_a, m_use);
+    update_max(s, m_use);
     bf16x8 pop[2][2];
-    softmax(s_a, m_use, pop);
-    pv(vbuf(j), pop);
+    softmax(s, m_use, pop);
+    pv(tbuf(i, kp), pop);
+  };
+  // one step: publish stage i+1 and refill the slot of stage i-1, form the scores of
+  // stage i+1 on the matrix core, then finish stage i
+  auto step = [&](int i, f32x16 (&s_cur)[2], uint32_t (&b_cur)[2], f32x16 (&s_nxt)[2],
+                  uint32_t (&b_nxt)[2]) __attribute__((always_inline)) {
+    if (i + 1 < n_st) {
+      wait_stage(i + 1, min(i + S - 2, n_st - 1));
+      fix_stage(i + 1);
+      __syncthreads();  // stage i+1 visible; every wavefront is done with stage i-1
+      if (i + S - 1 < n_st) issue_stage(i + S - 1);
+      prep(i + 1, s_nxt, b_nxt);
+    }
+    consume(i, s_cur, b_cur);
+  };
+
+  f32x16 s_a[2], s_b[2];
+  uint32_t b_a[2] = {0u, 0u}, b_b[2] = {0u, 0u};
+  if (n_st > 0) {
+    wait_stage(0, first - 1);
+    fix_stage(0);
+    __syncthreads();
+    prep(0, s_a, b_a);
+  }
+  for (int i = 0; i < n_st; i += 2) {
+    step(i, s_a, b_a, s_b, b_b);
+    if (i + 1 < n_st) step(i + 1, s_b, b_b, s_a, b_a);
   }
 
-  // ---- merge the four wavefronts through LDS (two passes of 64 dims)
+  // ---- combine the key phases (n_kp = 2: wavefront (rb, 1) hands its state to (rb, 0))
   float lsum[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -516,109 +556,115 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
     halves(l_run[c], y0, y1);
     lsum[c] = y0 + y1;
   }
-  __syncthreads();
-  float* obuf = reinterpret_cast<float*>(&s_k[0][0][0]);    // [wave][64 q][64 dims]
-  float2* mlb = reinterpret_cast<float2*>(&s_v[0][0][0]);   // [wave][64 q]
-  if (half == 0) {
+  if (n_kp == 2) {
+    __syncthreads();  // every wavefront is done with the ring
+    float* xo = reinterpret_cast<float*>(&s_ring[0][0]) + rb * (128 * 64 + 4 * 64);
+    if (kp == 1) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) mlb[wave * 64 + c * 32 + l32] = make_float2(m_run[c], lsum[c]);
-  }
-  Partial* part = nullptr;
-  if (p.splits > 1)
-    part = reinterpret_cast<Partial*>(static_cast<unsigned char*>(a.workspace) + p.partial_offset) +
-           (int64_t(unit) * p.qtiles + qt) * p.splits + split;
-  auto store_out = [&](int q, int dim0, float4 v) __attribute__((always_inline)) {
-    const int r = qt * kRowsWG + q;
-    if (r >= p.rows) return;
-    const int u = r / p.group, h = kvh * p.group + r % p.group;
-    bf16* o = static_cast<bf16*>(a.out) + ((int64_t(b) * N + u) * a.Hq + h) * kD + dim0;
-    const bf16x4 ov = {static_cast<bf16>(v.x), static_cast<bf16>(v.y), static_cast<bf16>(v.z),
-                       static_cast<bf16>(v.w)};
-    *reinterpret_cast<bf16x4*>(o) = ov;
-  };
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-  for (int dh = 0; dh < 2; ++dh) {
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int d2 = 0; d2 < 2; ++d2) {
+          for (int e = 0; e < 16; ++e) xo[((db * 2 + c) * 16 + e) * 64 + lane] = oacc[db][c][e];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x16& o = oacc[2 * dh + d2][c];
-          const float4 v = make_float4(o[4 * g4], o[4 * g4 + 1], o[4 * g4 + 2], o[4 * g4 + 3]);
-          const int q = c * 32 + l32, dl = 32 * d2 + 8 * g4 + 4 * half;
-          *reinterpret_cast<float4*>(obuf + (wave * 64 + q) * 64 + dl) = v;
-        }
+        xo[128 * 64 + c * 64 + lane] = m_run[c];
+        xo[128 * 64 + (2 + c) * 64 + lane] = lsum[c];
       }
     }
     __syncthreads();
-    for (int it = tid; it < 64 * 16; it += 256) {
-      const int q = it >> 4, d4 = it & 15;
-      float M = -INFINITY;
+    if (kp == 1) return;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mlb[w * 64 + q].x);
-      float L = 0.f;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < 2; ++c) {
+      const float m1 = xo[128 * 64 + c * 64 + lane], l1 = xo[128 * 64 + (2 + c) * 64 + lane];
+      const float M = fmaxf(m_run[c], m1);
+      const float w0 = m_run[c] == -INFINITY ? 0.f : exp2_fast(m_run[c] - M);
+      const float w1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - M);
+      lsum[c] = w0 * lsum[c] + w1 * l1;
+      m_run[c] = M;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float2 ml = mlb[w * 64 + q];
-        const float wt = M == -INFINITY ? 0.f : exp2_fast(ml.x - M);
-        L += wt * ml.y;
-        const float4 v = *reinterpret_cast<const float4*>(obuf + (w * 64 + q) * 64 + 4 * d4);
-        acc.x += wt * v.x;
-        acc.y += wt * v.y;
-        acc.z += wt * v.z;
-        acc.w += wt * v.w;
-      }
-      const int dim0 = 64 * dh + 4 * d4;
-      if (p.splits == 1) {
-        const float inv = 1.0f / L;
-        store_out(q, dim0, make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
-      } else {
-        *reinterpret_cast<float4*>(&part->o[q][dim0]) = acc;
-        if (dh == 0 && d4 == 0) {
-          part->m[q] = M;
-          part->l[q] = L;
-        }
-      }
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          oacc[db][c][e] = w0 * oacc[db][c][e] + w1 * xo[((db * 2 + c) * 16 + e) * 64 + lane];
     }
-    __syncthreads();
   }
-  if (p.splits == 1) return;
 
-  // ---- the last split to arrive merges all splits of this q-tile
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    int* counter = static_cast<int*>(a.workspace) + (unit * p.qtiles + qt);
-    const int prev = atomicAdd(counter, 1);
-    s_int = prev == p.splits - 1;
-    if (s_int) atomicExch(counter, 0);  // ready for the next call
-  }
-  __syncthreads();
-  if (!s_int) return;
-  __threadfence();
-  const Partial* base = part - split;
-  for (int it = tid; it < 64 * 32; it += 256) {
-    const int q = it >> 5, d4 = it & 31;
-    if (qt * kRowsWG + q >= p.rows) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, base[s].m[q]);
-    float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < p.splits; ++s) {
-      const float ms = base[s].m[q];
-      const float wt = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
-      L += wt * base[s].l[q];
-      const float4 v = *reinterpret_cast<const float4*>(&base[s].o[q][4 * d4]);
-      acc.x += wt * v.x;
-      acc.y += wt * v.y;
-      acc.z += wt * v.z;
-      acc.w += wt * v.w;
+  // ---- results: lane (half, l32) holds, for query row c * 32 + l32 of its 64-row block,
+  // dims 32 db + 8 g + 4 half + 0..3 in oacc[db][c][4 g .. 4 g + 3]
+  if (p.splits == 1) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r = row0 + c * 32 + l32;
+      if (r >= p.rows) continue;
+      const int u = r / p.group, h = kvh * p.group + r % p.group;
+      bf16* o = static_cast<bf16*>(a.out) + ((int64_t(b) * N + u) * a.Hq + h) * kD + 4 * half;
+      const float inv = 1.0f / lsum[c];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& v = oacc[db][c];
+          const bf16x4 ov = {static_cast<bf16>(v[4 * g] * inv), static_cast<bf16>(v[4 * g + 1] * inv),
+                             static_cast<bf16>(v[4 * g + 2] * inv), static_cast<bf16>(v[4 * g + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(o + 32 * db + 8 * g) = ov;
+        }
     }
-    const float inv = 1.0f / L;
-    store_out(q, 4 * d4, make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
+    return;
   }
+  const int64_t slot0 = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave;
+  float2* ml = static_cast<float2*>(a.workspace) + slot0;
+  float* po = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot0 * kD;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int q = c * 32 + l32;
+    if (half == 0) ml[q] = make_float2(m_run[c], lsum[c]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& v = oacc[db][c];
+        *reinterpret_cast<float4*>(po + q * kD + 32 * db + 8 * g + 4 * half) =
+            make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+      }
+  }
+}
+
+// Merge of the splits: thread (row, 4 dims) combines the splits' (m, l, O) partials.
+__global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
+  if (round_failed(p.status)) return;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int d4 = int(idx & 31);
+  const int64_t g = idx >> 5;  // (unit, query block, row of the block)
+  const int r = int(g % p.qrows);
+  const int64_t uq = g / p.qrows;
+  const int qb = int(uq % p.qblocks);
+  const int unit = int(uq / p.qblocks);
+  const int row = qb * p.qrows + r;
+  if (row >= p.rows) return;
+  const int64_t base = uq * p.splits * p.qrows + r;  // slot of split 0
+  float M = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.ml[base + int64_t(s) * p.qrows].x);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < p.splits; ++s) {
+    const int64_t slot = base + int64_t(s) * p.qrows;
+    const float2 ml = p.ml[slot];
+    const float wt = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - M);
+    L += wt * ml.y;
+    const float4 v = *reinterpret_cast<const float4*>(p.o + slot * kD + 4 * d4);
+    acc.x += wt * v.x;
+    acc.y += wt * v.y;
+    acc.z += wt * v.z;
+    acc.w += wt * v.w;
+  }
+  const float inv = 1.0f / L;
+  const int b = unit / p.Hkv, kvh = unit % p.Hkv;
+  const int u = row / p.group, h = kvh * p.group + row % p.group;
+  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kD + 4 * d4;
+  const bf16x4 ov = {static_cast<bf16>(acc.x * inv), static_cast<bf16>(acc.y * inv),
+                     static_cast<bf16>(acc.z * inv), static_cast<bf16>(acc.w * inv)};
+  *reinterpret_cast<bf16x4*>(o) = ov;
 }
 
 }  // namespace
@@ -640,14 +686,34 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   p.a = a;
   p.group = plan.group;
   p.rows = plan.rows;
-  p.qtiles = plan.qtiles;
+  p.n_kp = plan.n_kp;
+  p.qrows = plan.qrows;
+  p.qblocks = plan.qblocks;
   p.splits = plan.splits;
   p.xcd_map = plan.xcd_map ? 1 : 0;
-  p.partial_offset = int32_t(plan.partial_offset);
+  p.o_offset = int64_t(plan.o_offset);
   for (int j = 0; j < kD / 2; ++j) p.theta[j] = std::pow(a.rope_base, -2.0 * j / kD);
-  const unsigned grid = unsigned(int64_t(plan.units) * plan.splits * plan.qtiles);
-  return launch(reinterpret_cast<const void*>(&tree_attn_mfma_kernel), dim3(grid), dim3(256), 0,
-                stream, p, ev_start, ev_stop);
+  const unsigned grid = unsigned(int64_t(plan.units) * plan.splits * plan.qblocks);
+  const void* attn = reinterpret_cast<const void*>(&tree_attn_mfma_kernel);
+  if (plan.splits == 1) return launch(attn, dim3(grid), dim3(256), 0, stream, p, ev_start, ev_stop);
+  const medusa_status st = launch(attn, dim3(grid), dim3(256), 0, stream, p, ev_start, nullptr);
+  if (st != MEDUSA_OK) return st;
+  MergeArgs m{};
+  m.ml = static_cast<const float2*>(a.workspace);
+  m.o = reinterpret_cast<const float*>(static_cast<const unsigned char*>(a.workspace) + plan.o_offset);
+  m.out = a.out;
+  m.status = a.status;
+  m.Hq = a.Hq;
+  m.Hkv = a.Hkv;
+  m.N = a.N;
+  m.group = plan.group;
+  m.rows = plan.rows;
+  m.qrows = plan.qrows;
+  m.qblocks = plan.qblocks;
+  m.splits = plan.splits;
+  const int64_t threads = int64_t(plan.units) * plan.qblocks * plan.qrows * 32;
+  return launch(reinterpret_cast<const void*>(&tree_attn_merge_kernel),
+                dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, m, nullptr, ev_stop);
 }
 
 }  // namespace medusa

@@ -116,7 +116,8 @@ def test_host_rejects_bad_shapes():
 
 
 def test_repeated_calls_reuse_the_workspace():
-    """The split-merge counters live in the workspace and must be left at zero by every call."""
+    """A second call on the same workspace (holding the first call's split partials)
+    gives the same output bit for bit."""
     w = workloads.WORKLOADS["batched"]
     announce("attention twice on one workspace")
     lib, ora = compile_both(w)
@@ -128,5 +129,3 @@ def test_repeated_calls_reuse_the_workspace():
     run.kc.copy_(torch.from_numpy(x["k_cache"]).to("cuda", torch.bfloat16))
     assert run.run() == 0
     assert torch.equal(first, run.out)
-    counters = run.ws[:512].cpu().numpy()   # 4 bytes x 32 units x 4 q-tiles
-    assert (counters == 0).all()
