@@ -24,14 +24,20 @@ struct AttnArgs {
 };
 
 // Every sequence's staged rows [P_b, P_b + N) must lie inside the cache.  All
-// blocks evaluate the same condition, so they all store or none does.
+// blocks evaluate the same condition, so they all store or none does.  Each lane
+// checks one sequence per pass (a vector load, not a chain of scalar ones) and the
+// wavefront votes; the result is wave-uniform.
 __device__ __forceinline__ bool prefixes_fit(const AttnArgs& a) {
-  bool ok = true;
-  for (int b = 0; b < a.B; ++b) {
-    const int64_t P = a.prefix_len[b];
-    ok = ok && P >= 0 && P + a.N <= a.S_max;
+  const int lane = threadIdx.x & 63;
+  bool bad = false;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    if (b < a.B) {
+      const int64_t P = a.prefix_len[b];
+      bad |= (P < 0) | (P + a.N > a.S_max);
+    }
   }
-  return ok;
+  return __ballot(bad) == 0;
 }
 
 // Host-side dispatch helpers implemented next to the MFMA kernel.

@@ -12,33 +12,46 @@
 //    That block against a key tile is a dense contraction, so both products run
 //    on v_mfma_f32_32x32x16_bf16.  With 256 rows per unit each key byte feeds
 //    about as many flops as the matrix cores retire per HBM byte, so the kernel
-//    is balanced between HBM and MFMA and must overlap the two.
-//  * A workgroup takes up to 256 query rows of one unit (four wavefronts of 64
-//    rows) and one contiguous split of the unit's key tiles: the committed prefix
-//    followed by the staged rows.  Every key tile is fetched from HBM once, into
-//    LDS, and read there by all four wavefronts.  Query blocks of 128 rows or
-//    fewer use two key phases instead: wavefront pairs take alternate tiles.
-//  * The LDS holds a ring of eight 32-key tiles (K and V, 128 KiB) filled by
-//    direct global->LDS loads up to seven tiles ahead, so that about 100 KiB per
-//    CU is in flight, which is what HBM latency times bandwidth asks for.  Each
-//    wavefront loads its eight rows of every tile; one workgroup barrier per
-//    tile publishes the tile and frees the slot of the tile before.
+//    is balanced between HBM and MFMA and has to overlap the two.
+//  * A workgroup of eight wavefronts (two per SIMD, so that one wavefront's
+//    softmax overlaps the other's matrix work) takes 128 query rows of one unit,
+//    32 per wavefront, and one contiguous split of the unit's key tiles: the
+//    committed prefix followed by the staged rows.  The workgroup's two halves
+//    take alternate tiles (two key phases) and are combined through LDS at the
+//    end.  A unit of 256 rows has two query blocks; their workgroups run on one
+//    XCD, so each key tile comes from HBM once and from that XCD's L2 the second
+//    time, while the split partials that the merge kernel reads stay half the
+//    size they would be with one 256-row block and twice the splits.
+//  * The LDS holds a ring of eight 32-key tiles (K and V, 128 KiB): four stages
+//    of two tiles, filled by direct global->LDS loads up to three stages ahead.
+//    Each wavefront loads four rows of every tile of a stage; one workgroup
+//    barrier per stage publishes the stage and frees the slot of the stage before.
+//  * LDS tiles are XOR-swizzled so that both the 16-byte K-operand reads and the
+//    transposing V^T reads are free of bank conflicts on the 64-bank LDS.
 //  * Scores are formed transposed, S^T = K Q^T (K rows are the A operand,
 //    16-byte LDS reads), so the probability tile comes out of the accumulator
 //    already in the B-operand order of O^T = V^T P^T; V^T comes from LDS with
 //    the transposing ds_read_b64_tr_b16.  P is never shuffled.
-//  * Software pipeline per wavefront: the scores of tile j+1 run on the matrix
-//    core while the VALU does the softmax of tile j.
+//  * Software pipeline per wavefront: the scores of tile j+1 are formed on the
+//    matrix core before the softmax of tile j.
 //  * Online softmax in log2 units; the running maximum only moves when a tile
-//    exceeds it by more than 2^8, so the O rescale is almost never paid.
+//    exceeds it by more than 2^8, so the O rescale is almost never paid.  Row
+//    sums are taken over the bf16-rounded probabilities (the values P V uses)
+//    with packed bf16 dot products.
+//  * Everything the set-up reads from memory (status, prefix lengths, query
+//    rows, node depths, staged visibility words) is loaded at once, together
+//    with the first stage's tiles, and consumed before the rest of the ring is
+//    filled, so that no compiler-inserted wait drains the tile ring.
 //  * Staged keys are rotated to P + depth(u) in LDS by the wavefront that
-//    loaded them (binary64 phase angles kept as fp32 cos/sin), written to cache
-//    rows P + u by query block 0, and masked per lane with the ancestor bitmask.
+//    loaded them, written to cache rows P + u by query block 0, and masked per
+//    lane with the ancestor bitmask.  RoPE phases are reduced modulo 2 pi in
+//    binary64 and evaluated in fp32.
 //  * Splits of one query block are merged by a second, small kernel from
 //    (m, l, O) partials in the workspace; with a single split the first kernel
 //    writes the output itself.
 
 #include <cmath>
+#include <type_traits>
 
 #include "attn_common.h"
 
@@ -47,15 +60,20 @@ namespace {
 
 constexpr int kD = 128;          // head dimension
 constexpr int kTile = 32;        // keys per tile
-constexpr int kWaves = 4;
-constexpr int kRowsWave = 64;    // query rows per wavefront
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsWave = 32;    // query rows per wavefront
 constexpr int kRing = 8;         // tile buffers in LDS
 constexpr int kTileBytes = 2 * kTile * kD * 2;  // K then V of one tile
 constexpr int kTableDepth = 32;  // RoPE phases kept in LDS; deeper trees are rejected
-constexpr int kDepthLds = 8192;  // node depths cached in LDS (bytes); later nodes read HBM
+constexpr int kDepthLds = 4096;  // node depths cached in LDS (bytes); later nodes read memory
+constexpr int kMaskLds = 8;      // staged tiles whose visibility words are kept in LDS
 constexpr int kTargetWGs = 256;  // one workgroup per compute unit
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr double kTwoPiHi = 6.283185307179586;         // 2 pi = hi + lo
+constexpr double kTwoPiLo = 2.4492935982947064e-16;
+constexpr double kInvTwoPi = 0.15915494309189535;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -67,8 +85,8 @@ struct MfmaArgs {
   AttnArgs a;
   int32_t group;     // Hq / Hkv
   int32_t rows;      // N * group query rows per unit
-  int32_t n_kp;      // key phases: 1 (four wavefronts share every tile) or 2
-  int32_t qrows;     // query rows per workgroup: 64 * 4 / n_kp
+  int32_t n_kp;      // key phases: 1 (all eight wavefronts share every tile) or 2
+  int32_t qrows;     // query rows per workgroup: 32 * 8 / n_kp
   int32_t qblocks;   // ceil(rows / qrows)
   int32_t splits;    // workgroups sharing one query block's keys
   int32_t xcd_map;   // keep the query blocks of one (unit, split) on one XCD
@@ -95,7 +113,7 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
   p.units = B * Hkv;
   p.group = Hq / Hkv;
   p.rows = N * p.group;
-  p.n_kp = p.rows > 2 * kRowsWave ? 1 : 2;
+  p.n_kp = 2;
   p.qrows = kRowsWave * kWaves / p.n_kp;
   p.qblocks = (p.rows + p.qrows - 1) / p.qrows;
   const int32_t wgs = p.units * p.qblocks;
@@ -112,10 +130,14 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
   return p;
 }
 
-// byte offset of (row, 16-byte chunk) in a 32 x 256-byte matrix; chunks are
-// XOR-swizzled by row so that column reads spread over the LDS banks
+// Byte offset of (row, 16-byte chunk) in a 32 x 256-byte matrix.  Chunks are XOR-swizzled
+// by a key that is a bijection over any 16 aligned rows (so the 16-byte K-operand reads
+// of 16 rows hit 16 distinct bank groups of the 64-bank LDS) and whose high two bits differ
+// within every aligned group of 4 rows (so the transposing V^T reads, 4 rows x 4 chunks per
+// 32 lanes, do as well): both read patterns are free of bank conflicts.
+__device__ __forceinline__ int swz_key(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 256 + ((chunk ^ (row & 15)) << 4);
+  return row * 256 + ((chunk ^ swz_key(row)) << 4);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -151,31 +173,30 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 }
 
 // wait until at most n of this wavefront's vector memory operations are outstanding
-// (n rounded down to a multiple of 4, which only makes the wait stricter)
+// (n rounded down to an even count, which only makes the wait stricter)
 __device__ __forceinline__ void wait_vm(int n) {
-  switch (n >= 24 ? 6 : n >> 2) {
-    case 6: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+  switch (n >= 14 ? 7 : n >> 1) {
+    case 7: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
 
-__global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
+// an empty use of a register, so that the compiler completes the load producing it here
+__device__ __forceinline__ void touch(uint32_t v) { asm volatile("" ::"v"(v)); }
+
+__global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   const AttnArgs& a = p.a;
-  if (round_failed(a.status)) return;
-  if (!prefixes_fit(a)) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) raise_status(a.status, MEDUSA_ECAPACITY);
-    return;
-  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5, l32 = lane & 31;
   const int n_kp = p.n_kp;
-  const int kp = wave % n_kp, rb = wave / n_kp;  // key phase, 64-row block
+  const int kp = wave % n_kp, rb = wave / n_kp;  // key phase, 32-row block
 
   // ---- this workgroup's (sequence, kv head, split, query block)
   int grp, qb;
@@ -189,19 +210,44 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   }
   const int unit = grp / p.splits, split = grp % p.splits;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
-  const int P = a.prefix_len[b];
   const int N = a.N;
+  const int n_stg = (N + kTile - 1) / kTile;
 
   __shared__ __attribute__((aligned(16))) unsigned char s_ring[kRing][kTileBytes];
   __shared__ float2 s_cs[kTableDepth][kD / 2];
   __shared__ unsigned char s_dep[kDepthLds];
-  __shared__ int s_int;
+  __shared__ uint32_t s_mw[kWaves][kMaskLds][kRowsWave];
+  __shared__ int s_bad[kWaves];
+
+  // ---- set-up loads, independent of each other and issued together: every address is
+  // clamped into range instead of branching, so that no load waits for another.  This
+  // lane's query row is row0 + l32 of the unit: node u_q, head h_q.
+  const bool failed = round_failed(a.status);
+  const int64_t P_lane = a.prefix_len[min(lane, a.B - 1)];  // sequences 0..63, checked below
+  const int P = a.prefix_len[b];                             // scalar
+  const int row0 = qb * p.qrows + rb * kRowsWave;
+  const int rq = row0 + l32;
+  const bool live = rq < p.rows;
+  const int u_q = live ? rq / p.group : 0;
+  const int h_q = kvh * p.group + (live ? rq % p.group : 0);
+  const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t(b) * N + u_q) * a.Hq + h_q) * kD;
+  uint4 raw[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) raw[s] = *reinterpret_cast<const uint4*>(qr + 16 * s + 8 * half);
+  const int dep_q = a.depth[u_q];
+  const int dep0 = a.depth[min(tid, N - 1)];
+  const double theta = p.theta[tid % (kD / 2)];  // the frequency of this thread's phase entries
+  // visibility of staged tile k (nodes 32 k .. 32 k + 31) for this lane's query node
+  uint64_t mword[kMaskLds / 2];
+#pragma unroll
+  for (int k = 0; k < kMaskLds / 2; ++k)
+    mword[k] = a.mask[int64_t(u_q) * a.mask_words + min(k, a.mask_words - 1)];
 
   // ---- key tiles of the unit: n_pre prefix tiles (the last one may be partial), then the
   // staged tiles.  Stage i of this split holds tiles (s_lo + i) * n_kp + k, k < n_kp, in
   // ring slot i % S.
   const int n_pre = (P + kTile - 1) / kTile;
-  const int T = n_pre + (N + kTile - 1) / kTile;
+  const int T = n_pre + n_stg;
   const int n_stages = (T + n_kp - 1) / n_kp;
   const int s_lo = int(int64_t(split) * n_stages / p.splits);
   const int n_st = int(int64_t(split + 1) * n_stages / p.splits) - s_lo;
@@ -221,45 +267,30 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
     return s_ring[(i & (S - 1)) * n_kp + k];
   };
 
-  // Rows 8 w .. 8 w + 7 of one tile's K and V by direct global->LDS loads (wavefront w,
-  // two instructions of four rows per matrix): lane l lands at byte 1024 i + 16 l of the
-  // matrix, i.e. row 4 i + l / 16, stored chunk l % 16, and fetches logical chunk
-  // (l % 16) ^ (row % 16), so that the buffer holds the layout swz() reads back.
-  uint32_t poff[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int rt = 4 * (2 * wave + h) + (lane >> 4);
-    poff[h] = uint32_t(rt * 256 + (((lane & 15) ^ (rt & 15)) << 4));
-  }
+  // Rows 4 w .. 4 w + 3 of one tile's K and V by direct global->LDS loads (wavefront w,
+  // one instruction per matrix): lane l lands at byte 1024 w + 16 l of the matrix, i.e.
+  // row 4 w + l / 16, stored chunk l % 16, and fetches logical chunk (l % 16) ^ key(row),
+  // so that the buffer holds the layout swz() reads back.
+  const int rt_dma = 4 * wave + (lane >> 4);
+  const int chunk_dma = (lane & 15) ^ swz_key(rt_dma);  // logical chunk this lane fetches
+  const uint32_t poff = uint32_t(rt_dma * 256 + (chunk_dma << 4));
   auto issue_tile = [&](int t, unsigned char* buf) __attribute__((always_inline)) {
-    const uint32_t lds = lds_addr(buf) + 2048 * wave;
+    const uint32_t lds = lds_addr(buf) + 1024 * wave;
     if ((t + 1) * kTile <= P) {  // full prefix tile
       const int64_t off = int64_t(t) * kTile * kD;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        dma16(kc + off, poff[h], lds + 1024 * h);
-        dma16(vc + off, poff[h], lds + 8192 + 1024 * h);
-      }
+      dma16(kc + off, poff, lds);
+      dma16(vc + off, poff, lds + 8192);
     } else if (t < n_pre) {  // the partial prefix tile: rows past P repeat row 0
       const int64_t off = int64_t(t) * kTile * kD;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rt = 4 * (2 * wave + h) + (lane >> 4);
-        const int r = t * kTile + rt < P ? rt : 0;
-        const uint32_t o = uint32_t(r * 256 + (((lane & 15) ^ (rt & 15)) << 4));
-        dma16(kc + off, o, lds + 1024 * h);
-        dma16(vc + off, o, lds + 8192 + 1024 * h);
-      }
+      const int r = t * kTile + rt_dma < P ? rt_dma : 0;
+      const uint32_t o = uint32_t(r * 256 + (chunk_dma << 4));
+      dma16(kc + off, o, lds);
+      dma16(vc + off, o, lds + 8192);
     } else {  // staged rows from k_new / v_new; rows past the tree repeat node 0
-      const int v0 = (t - n_pre) * kTile;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rt = 4 * (2 * wave + h) + (lane >> 4);
-        const int u = v0 + rt < N ? v0 + rt : 0;
-        const uint32_t o = uint32_t((u * a.Hkv * kD + 8 * ((lane & 15) ^ (rt & 15))) * 2);
-        dma16(kn, o, lds + 1024 * h);
-        dma16(vn, o, lds + 8192 + 1024 * h);
-      }
+      const int u = (t - n_pre) * kTile + rt_dma;
+      const uint32_t o = uint32_t(((u < N ? u : 0) * a.Hkv * kD + 8 * chunk_dma) * 2);
+      dma16(kn, o, lds);
+      dma16(vn, o, lds + 8192);
     }
   };
   auto issue_stage = [&](int i) __attribute__((always_inline)) {
@@ -269,84 +300,117 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
     }
   };
   // wait until this wavefront's loads of stage i have landed, stages up to `last` having
-  // been issued (four loads per tile)
+  // been issued (two loads per tile)
   auto wait_stage = [&](int i, int last) __attribute__((always_inline)) {
-    wait_vm(last > i ? 4 * (tile_end(last) - tile_end(i)) : 0);
+    wait_vm(last > i ? 2 * (tile_end(last) - tile_end(i)) : 0);
   };
 
-  // fill the ring, all but one slot, before the latency-bound set-up below
-  const int first = min(S - 1, n_st);
-  for (int i = 0; i < first; ++i) issue_stage(i);
+  // The first stage's tile loads need only P (a scalar load): issue them now, while the
+  // set-up loads above are in flight, unless P is out of range (checked for every
+  // sequence below, which then raises the error).
+  if (P >= 0 && P <= a.S_max - N && n_st > 0) issue_stage(0);
 
-  // ---- node depths (LDS copy) and the RoPE phases (cos, sin) of positions P + d for
-  // every depth d of the tree
-  if (tid == 0) s_int = 0;
-  __syncthreads();
-  int dmax = 0;
-  for (int i = tid; i < N; i += 256) {
+  // consume them all; the first stage's tile loads, issued above, complete with them, so
+  // that no tile load is in flight at the early exits below
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    touch(raw[s].x);
+    touch(raw[s].y);
+    touch(raw[s].z);
+    touch(raw[s].w);
+  }
+  if (half == 0) {
+#pragma unroll
+    for (int k = 0; k < kMaskLds; ++k)
+      s_mw[wave][k][l32] = k < n_stg ? uint32_t(mword[k >> 1] >> (32 * (k & 1))) : 0u;
+  }
+  touch(uint32_t(dep_q));
+  touch(uint32_t(dep0));
+  touch(uint32_t(__double_as_longlong(theta)));
+  touch(uint32_t(__double_as_longlong(theta) >> 32));
+  touch(uint32_t(P_lane));
+  wait_vm(0);
+  if (failed) return;
+  // every sequence's staged rows [P_b, P_b + N) must lie inside the cache; all blocks
+  // evaluate the same condition, so that they all store or none does
+  bool unfit = lane < a.B && (P_lane < 0 || P_lane + N > a.S_max);
+  for (int b2 = 64 + lane; b2 < a.B; b2 += 64) {  // batches of more than 64 sequences
+    const int64_t Pb = a.prefix_len[b2];
+    unfit = unfit || Pb < 0 || Pb + N > a.S_max;
+  }
+  if (__ballot(unfit)) {
+    if (blockIdx.x == 0 && tid == 0) raise_status(a.status, MEDUSA_ECAPACITY);
+    return;
+  }
+  if (!live) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) raw[s] = make_uint4(0, 0, 0, 0);
+  }
+  bool bad = tid < N && (dep0 < 0 || dep0 >= kTableDepth);
+  if (tid < N && tid < kDepthLds) s_dep[tid] = static_cast<unsigned char>(dep0);
+  for (int i = tid + kThreads; i < N; i += kThreads) {  // trees of more than 512 nodes
     const int d = a.depth[i];
-    dmax = max(dmax, d);
+    bad = bad || d < 0 || d >= kTableDepth;
     if (i < kDepthLds) s_dep[i] = static_cast<unsigned char>(d);
   }
-  atomicMax(&s_int, dmax);
+
+  // fill the rest of the ring, all but one slot
+  const int first = min(S - 1, n_st);
+  for (int i = 1; i < first; ++i) issue_stage(i);
+
+  // ---- RoPE phases (cos, sin) of positions P + d for every depth d < 32: the angle is
+  // formed and reduced modulo 2 pi in binary64, then evaluated in fp32.  Thread tid
+  // fills entries (d, tid % 64) for d = tid / 64 + 8 k.
+  static_assert(kThreads % (kD / 2) == 0, "a thread's phase entries share one frequency");
+  for (int i = tid; i < kTableDepth * (kD / 2); i += kThreads) {
+    const int d = i / (kD / 2), j = i % (kD / 2);
+    const double x = double(P + d) * theta;
+    const double k = rint(x * kInvTwoPi);
+    const float r = float(fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, x)));
+    float sn, cs;
+    sincosf(r, &sn, &cs);
+    s_cs[d][j] = make_float2(cs, sn);
+  }
+  if (lane == 0) s_bad[wave] = 0;
+  if (__ballot(bad) != 0 && lane == 0) s_bad[wave] = 1;
   __syncthreads();
-  dmax = s_int;
-  if (dmax >= kTableDepth) {  // uniform: every block sees the same tree
-    wait_vm(0);               // no load may still target LDS when the block exits
+  int any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) any_bad |= s_bad[w];
+  if (any_bad) {  // a node deeper than the phase table: uniform over the workgroup
+    wait_vm(0);   // no load may still target LDS when the block exits
     if (blockIdx.x == 0 && tid == 0) raise_status(a.status, MEDUSA_EUNSUPPORTED);
     return;
   }
-  for (int i = tid; i < (dmax + 1) * (kD / 2); i += 256) {
-    const int d = i / (kD / 2), j = i % (kD / 2);
-    double sn, cs;
-    sincos(double(P + d) * p.theta[j], &sn, &cs);
-    s_cs[d][j] = make_float2(float(cs), float(sn));
-  }
-  __syncthreads();
-  auto depth_of = [&](int u) __attribute__((always_inline)) -> int {
-    return u < kDepthLds ? int(s_dep[u]) : a.depth[u];
-  };
 
-  // ---- this wavefront's 64 query rows: rotated, scaled to log2 units, bf16 B operands;
-  // lane holds query column l32 of column block c, dims 16 s + 8 half + e (e < 8)
-  const int row0 = qb * p.qrows + rb * kRowsWave;
+  // ---- this wavefront's 32 query rows: rotated, scaled to log2 units, bf16 B operands;
+  // lane holds query column l32, dims 16 s + 8 half + e (e < 8)
   const float qscale = kLog2e / sqrtf(float(kD));
-  bf16x8 qop[2][8];
-  int qnode[2];
+  bf16x8 qop[8];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int r = row0 + c * 32 + l32;
-    const bool live = r < p.rows;
-    const int u = live ? r / p.group : 0;
-    const int h = kvh * p.group + (live ? r % p.group : 0);
-    qnode[c] = u;
-    const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t(b) * N + u) * a.Hq + h) * kD;
-    uint4 raw[8];
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8 lo = __builtin_bit_cast(bf16x8, raw[s]);
+    const bf16x8 hi = __builtin_bit_cast(bf16x8, raw[s + 4]);
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      raw[s] = live ? *reinterpret_cast<const uint4*>(qr + 16 * s + 8 * half) : make_uint4(0, 0, 0, 0);
-    const int dep = depth_of(u);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 lo = __builtin_bit_cast(bf16x8, raw[s]);
-      const bf16x8 hi = __builtin_bit_cast(bf16x8, raw[s + 4]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 cs = s_cs[dep][16 * s + 8 * half + e];
-        const float x1 = float(lo[e]), x2 = float(hi[e]);
-        qop[c][s][e] = static_cast<bf16>((x1 * cs.x - x2 * cs.y) * qscale);
-        qop[c][s + 4][e] = static_cast<bf16>((x2 * cs.x + x1 * cs.y) * qscale);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float2 cs = s_cs[dep_q][16 * s + 8 * half + e];
+      const float x1 = float(lo[e]), x2 = float(hi[e]);
+      qop[s][e] = static_cast<bf16>((x1 * cs.x - x2 * cs.y) * qscale);
+      qop[s + 4][e] = static_cast<bf16>((x2 * cs.x + x1 * cs.y) * qscale);
     }
   }
 
-  // Staged rows of one tile that this wavefront loaded (rows 8 w .. 8 w + 7): rotate K in
-  // place to P + depth(u); query block 0 also stores K~ and V to cache rows P + u.  Lane l
-  // takes row 8 w + l / 8 and the chunk pair (l % 8, l % 8 + 8), i.e. dims j and j + 64.
-  auto fix_staged = [&](int t, unsigned char* buf) __attribute__((always_inline)) {
-    const int rt = 8 * wave + (lane >> 3), c = lane & 7;
+  // Staged rows of one tile that this wavefront loaded (rows 4 w .. 4 w + 3): rotate K in
+  // place to P + depth(u); query block 0 also stores K~ and V to cache rows P + u.  Lane
+  // l < 32 takes row 4 w + l / 8 and the chunk pair (l % 8, l % 8 + 8), i.e. dims j, j + 64.
+  // Depths come from the LDS copy; trees too large for it read them from memory, in a
+  // separate instantiation so that the common path carries no wait for that load.
+  auto fix_staged = [&](int t, unsigned char* buf, auto depth_in_memory) __attribute__((always_inline)) {
+    if (lane >= 32) return;
+    const int rt = 4 * wave + (lane >> 3), c = lane & 7;
     const int uu = (t - n_pre) * kTile + rt;
-    const int dep = depth_of(uu < N ? uu : 0);
+    const int u = uu < N ? uu : 0;
+    const int dep = decltype(depth_in_memory)::value ? a.depth[u] : int(s_dep[u]);
     uint4* px = reinterpret_cast<uint4*>(buf + swz(rt, c));
     uint4* py = reinterpret_cast<uint4*>(buf + swz(rt, c + 8));
     const bf16x8 xv = __builtin_bit_cast(bf16x8, *px);
@@ -374,157 +438,182 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   auto fix_stage = [&](int i) __attribute__((always_inline)) {
     for (int k = 0; k < n_kp; ++k) {
       const int t = tile_start(i) + k;
-      if (t >= n_pre && t < T) fix_staged(t, tbuf(i, k));
-    }
-  };
-
-  // S^T = K Q^T for one tile: 32 keys x 64 query columns
-  auto qk = [&](const unsigned char* kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[c][e] = 0.f;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + swz(l32, 2 * st + half)));
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[0][st], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[1][st], s[1], 0, 0, 0);
-    }
-  };
-  // visibility bits of a tile's 32 keys for query column block c (bit m = key m of the
-  // tile); all ones for a full prefix tile
-  auto tile_bits = [&](int t, uint32_t (&bits)[2]) __attribute__((always_inline)) {
-    if (t < n_pre) {
-      const int nvalid = P - t * kTile;
-      bits[0] = bits[1] = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
-    } else {
-      const int v0 = (t - n_pre) * kTile;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint64_t word = a.mask[int64_t(qnode[c]) * a.mask_words + (v0 >> 6)];
-        bits[c] = uint32_t(word >> (v0 & 63));
+      if (t >= n_pre && t < T) {
+        if (N <= kDepthLds)
+          fix_staged(t, tbuf(i, k), std::false_type{});
+        else
+          fix_staged(t, tbuf(i, k), std::true_type{});
       }
     }
   };
 
-  f32x16 oacc[4][2];
+  // K operands of one tile for S^T = K Q^T, k-steps 4 kh .. 4 kh + 3: row l32, logical
+  // chunk 2 st + half.  With the swizzle its byte offset is kbase ^ (32 st), kbase being
+  // that of st = 0; the tile base (a multiple of 16 KiB) is added first, which leaves the
+  // XORed bits alone and keeps the per-lane offsets from being hoisted out of the loop.
+  const uint32_t kbase = uint32_t(swz(l32, half));
+  auto read_k = [&](const unsigned char* tb, int kh, bf16x8 (&kop)[4]) __attribute__((always_inline)) {
+    const uint32_t b = lds_addr(tb) + kbase;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t addr = b ^ uint32_t(32 * (4 * kh + j));
+      kop[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(addr));
+    }
+  };
+  // S^T = K Q^T for one tile, k-steps 4 kh .. 4 kh + 3 (32 keys x 32 query columns)
+  auto qk = [&](int kh, const bf16x8 (&kop)[4], f32x16& s) __attribute__((always_inline)) {
+    if (kh == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[j], qop[4 * kh + j], s, 0, 0, 0);
+  };
+  // visibility bits of a tile's 32 keys for this lane's query row (bit m = key m of the
+  // tile); all ones for a full prefix tile
+  auto tile_bits = [&](int t) __attribute__((always_inline)) -> uint32_t {
+    if (t < n_pre) {
+      const int nvalid = P - t * kTile;
+      return nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+    }
+    const int ks = t - n_pre;
+    if (ks < kMaskLds) {
+      // the lane index passes through an empty asm so that this rarely used address is
+      // formed here, not kept (and spilled) across the loop
+      int l = l32;
+      asm volatile("" : "+v"(l));
+      return s_mw[wave][ks][l];
+    }
+    // wide trees: read the word from memory (the wait for it also drains the tile ring)
+    return uint32_t(a.mask[int64_t(u_q) * a.mask_words + (ks >> 1)] >> (32 * (ks & 1)));
+  };
+
+  f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][c][e] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
-  // per-lane LDS offsets of the V^T operand reads: 32-dim block db, key group h of the
-  // 16-key step; the step t2 adds 16 rows (4096 bytes) to both
+  // Per-lane LDS offsets of the V^T operand reads (in the V half of a tile buffer): lane
+  // (gq, gi) supplies row key0 + 8 h, dims 32 db + 16 (gq % 2) + 4 (gi % 4) .. + 3.  The
+  // chunk index is 4 db + c with c < 4 and the row's swizzle key is 4 (row % 4) + k, so the
+  // swizzled offset is vbase[h] ^ (64 db) with vbase[h] that of db = 0; the 16-key step t2
+  // adds 16 rows (4096 bytes).
   const int gq = lane >> 4, gi = lane & 15;
-  int voff[4][2];
+  uint32_t vbase[2];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int dim = db * 32 + 16 * (gq & 1) + 4 * (gi & 3);
-    const int key0 = 4 * (gq >> 1) + (gi >> 2);
-    voff[db][0] = 8192 + swz(key0, dim >> 3) + ((dim & 4) << 1);
-    voff[db][1] = 8192 + swz(key0 + 8, dim >> 3) + ((dim & 4) << 1);
+  for (int h = 0; h < 2; ++h) {
+    const int dim = 16 * (gq & 1) + 4 * (gi & 3);
+    const int row = 4 * (gq >> 1) + (gi >> 2) + 8 * h;
+    vbase[h] = uint32_t(8192 + swz(row, dim >> 3) + ((dim & 4) << 1));
   }
-
-  // running-max update of one tile's scores; rescales O and l in the rare case it moves
-  auto update_max = [&](f32x16 (&sc)[2], float (&m_use)[2]) __attribute__((always_inline)) {
-    bool grow_any = false;
-    bool grow[2];
-    float tmax[2];
+  // V^T operands of one tile for the 64 output dims of half dh: 32-dim block 2 dh + j,
+  // 16-key step t2
+  auto read_v = [&](const unsigned char* tb, int dh, bf16x8 (&vop)[2][2]) __attribute__((always_inline)) {
+    const uint32_t t0 = lds_addr(tb);
+    const uint32_t b0 = t0 + vbase[0], b1 = t0 + vbase[1];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float x = fmaxf(fmaxf(sc[c][0], sc[c][1]), fmaxf(sc[c][2], sc[c][3]));
-#pragma unroll
-      for (int e = 4; e < 16; e += 2) x = fmaxf(x, fmaxf(sc[c][e], sc[c][e + 1]));
-      float y0, y1;
-      halves(x, y0, y1);
-      tmax[c] = fmaxf(y0, y1);
-      grow[c] = tmax[c] > m_run[c] + kRescaleSlack;
-      grow_any = grow_any || grow[c];
-    }
-    if (__ballot(grow_any)) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float m_new = grow[c] ? tmax[c] : m_run[c];
-        const float corr = grow[c] ? exp2_fast(m_run[c] - m_new) : 1.0f;
-        l_run[c] *= corr;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][c][e] *= corr;
-        m_run[c] = m_new;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) m_use[c] = m_run[c] == -INFINITY ? 0.f : m_run[c];
-  };
-  // probabilities of one tile (in place), their row sums, and the bf16 B operands of P^T
-  auto softmax = [&](f32x16 (&sc)[2], const float (&m_use)[2], bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = exp2_fast(sc[c][e] - m_use[c]);
-        sc[c][e] = pe;
-        psum += pe;
-      }
-      l_run[c] += psum;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pop[c][t2][e] = static_cast<bf16>(sc[c][8 * t2 + e]);
-    }
-  };
-  // O^T += V^T P^T: k index 8 h + e of a 16-key step pairs with key 16 t2 + 8 (e / 4) +
-  // 4 h + e % 4, exactly the order in which the score accumulator holds P
-  auto pv = [&](const unsigned char* tb, const bf16x8 (&pop)[2][2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t x = uint32_t(64 * (2 * dh + j));
+      const uint32_t a0 = b0 ^ x, a1 = b1 ^ x;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb + voff[db][0] + 4096 * t2));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb + voff[db][1] + 4096 * t2));
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[0][t2], oacc[db][0], 0, 0, 0);
-        oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[1][t2], oacc[db][1], 0, 0, 0);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t(a0 + 4096 * t2)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t(a1 + 4096 * t2)));
+        vop[j][t2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
   };
+  // O^T += V^T P^T for output half dh: k index 8 h + e of a 16-key step pairs with key
+  // 16 t2 + 8 (e / 4) + 4 h + e % 4, exactly the order in which the score accumulator holds P
+  auto pv = [&](int dh, const bf16x8 (&vop)[2][2], const bf16x8 (&pop)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+        oacc[2 * dh + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j][t2], pop[t2], oacc[2 * dh + j], 0, 0, 0);
+  };
 
-  // this wavefront's tile of stage i: visibility bits and scores
-  auto prep = [&](int i, f32x16 (&s)[2], uint32_t (&bits)[2]) __attribute__((always_inline)) {
+  // running-max update of one tile's scores; rescales O and l in the rare case it moves.
+  // Returns the reference the probabilities are taken against.
+  auto update_max = [&](const f32x16& sc) __attribute__((always_inline)) -> float {
+    float x = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+#pragma unroll
+    for (int e = 4; e < 16; e += 2) x = fmaxf(x, fmaxf(sc[e], sc[e + 1]));
+    float y0, y1;
+    halves(x, y0, y1);
+    const float tmax = fmaxf(y0, y1);
+    const bool grow = tmax > m_run + kRescaleSlack;
+    if (__ballot(grow)) {
+      const float m_new = grow ? tmax : m_run;
+      const float corr = grow ? exp2_fast(m_run - m_new) : 1.0f;
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
+      m_run = m_new;
+    }
+    return m_run == -INFINITY ? 0.f : m_run;
+  };
+  // probabilities of one tile as the bf16 B operands of P^T; the row sum is taken over
+  // the rounded values (the ones P V uses) with packed bf16 dot products
+  auto probs = [&](const f32x16& sc, float m_use, bf16x8 (&pop)[2]) __attribute__((always_inline)) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pop[t2][e] = static_cast<bf16>(exp2_fast(sc[8 * t2 + e] - m_use));
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pop[t2][e], pop[t2][e + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+      }
+  };
+
+  // prep: this wavefront's tile of stage i -- visibility bits and scores
+  auto prep = [&](int i, f32x16& s, uint32_t& bits) __attribute__((always_inline)) {
     const int t = tile_start(i) + kp;
     if (t < T) {
-      tile_bits(t, bits);
-      qk(tbuf(i, kp), s);
+      bits = tile_bits(t);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        bf16x8 kop[4];
+        read_k(tbuf(i, kp), kh, kop);
+        qk(kh, kop, s);
+      }
     }
   };
-  // masking, softmax and PV of this wavefront's tile of stage i
-  auto consume = [&](int i, f32x16 (&s)[2], const uint32_t (&bits)[2]) __attribute__((always_inline)) {
+  // consume: masking, softmax and PV of this wavefront's tile of stage i
+  auto consume = [&](int i, f32x16& s, uint32_t bits) __attribute__((always_inline)) {
     const int t = tile_start(i) + kp;
     if (t >= T) return;
     if (t >= n_pre - 1) {  // the last prefix tile or a staged tile
+      // element e holds key 8 (e / 4) + 4 half + e % 4; shifting by 4 half first leaves
+      // compile-time bit positions
+      const uint32_t bh = bits >> (4 * half);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = 8 * (e >> 2) + 4 * half + (e & 3);
-          if (!((bits[c] >> m) & 1u)) s[c][e] = -INFINITY;
-        }
+      for (int e = 0; e < 16; ++e)
+        if (!((bh >> (8 * (e >> 2) + (e & 3))) & 1u)) s[e] = -INFINITY;
     }
-    float m_use[2];
-    update_max(s, m_use);
-    bf16x8 pop[2][2];
-    softmax(s, m_use, pop);
-    pv(tbuf(i, kp), pop);
+    const float m_use = update_max(s);
+    bf16x8 pop[2];
+    probs(s, m_use, pop);
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh) {
+      bf16x8 vop[2][2];
+      read_v(tbuf(i, kp), dh, vop);
+      pv(dh, vop, pop);
+    }
   };
   // one step: publish stage i+1 and refill the slot of stage i-1, form the scores of
   // stage i+1 on the matrix core, then finish stage i
-  auto step = [&](int i, f32x16 (&s_cur)[2], uint32_t (&b_cur)[2], f32x16 (&s_nxt)[2],
-                  uint32_t (&b_nxt)[2]) __attribute__((always_inline)) {
+  auto step = [&](int i, f32x16& s_cur, uint32_t& b_cur, f32x16& s_nxt, uint32_t& b_nxt)
+      __attribute__((always_inline)) {
     if (i + 1 < n_st) {
       wait_stage(i + 1, min(i + S - 2, n_st - 1));
       fix_stage(i + 1);
@@ -535,102 +624,86 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
     consume(i, s_cur, b_cur);
   };
 
-  f32x16 s_a[2], s_b[2];
-  uint32_t b_a[2] = {0u, 0u}, b_b[2] = {0u, 0u};
+  f32x16 s_cur, s_nxt;
+  uint32_t b_cur = 0u, b_nxt = 0u;
   if (n_st > 0) {
     wait_stage(0, first - 1);
     fix_stage(0);
     __syncthreads();
-    prep(0, s_a, b_a);
+    prep(0, s_cur, b_cur);
   }
-  for (int i = 0; i < n_st; i += 2) {
-    step(i, s_a, b_a, s_b, b_b);
-    if (i + 1 < n_st) step(i + 1, s_b, b_b, s_a, b_a);
+  for (int i = 0; i < n_st; ++i) {
+    step(i, s_cur, b_cur, s_nxt, b_nxt);
+    s_cur = s_nxt;
+    b_cur = b_nxt;
   }
 
   // ---- combine the key phases (n_kp = 2: wavefront (rb, 1) hands its state to (rb, 0))
-  float lsum[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  float lsum;
+  {
     float y0, y1;
-    halves(l_run[c], y0, y1);
-    lsum[c] = y0 + y1;
+    halves(l_run, y0, y1);
+    lsum = y0 + y1;
   }
   if (n_kp == 2) {
     __syncthreads();  // every wavefront is done with the ring
-    float* xo = reinterpret_cast<float*>(&s_ring[0][0]) + rb * (128 * 64 + 4 * 64);
+    float* xo = reinterpret_cast<float*>(&s_ring[0][0]) + rb * (64 * 64 + 2 * 64);
     if (kp == 1) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) xo[((db * 2 + c) * 16 + e) * 64 + lane] = oacc[db][c][e];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        xo[128 * 64 + c * 64 + lane] = m_run[c];
-        xo[128 * 64 + (2 + c) * 64 + lane] = lsum[c];
-      }
+        for (int e = 0; e < 16; ++e) xo[(db * 16 + e) * 64 + lane] = oacc[db][e];
+      xo[64 * 64 + lane] = m_run;
+      xo[64 * 64 + 64 + lane] = lsum;
     }
     __syncthreads();
     if (kp == 1) return;
+    const float m1 = xo[64 * 64 + lane], l1 = xo[64 * 64 + 64 + lane];
+    const float M = fmaxf(m_run, m1);
+    const float w0 = m_run == -INFINITY ? 0.f : exp2_fast(m_run - M);
+    const float w1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - M);
+    lsum = w0 * lsum + w1 * l1;
+    m_run = M;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const float m1 = xo[128 * 64 + c * 64 + lane], l1 = xo[128 * 64 + (2 + c) * 64 + lane];
-      const float M = fmaxf(m_run[c], m1);
-      const float w0 = m_run[c] == -INFINITY ? 0.f : exp2_fast(m_run[c] - M);
-      const float w1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - M);
-      lsum[c] = w0 * lsum[c] + w1 * l1;
-      m_run[c] = M;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          oacc[db][c][e] = w0 * oacc[db][c][e] + w1 * xo[((db * 2 + c) * 16 + e) * 64 + lane];
-    }
+      for (int e = 0; e < 16; ++e) oacc[db][e] = w0 * oacc[db][e] + w1 * xo[(db * 16 + e) * 64 + lane];
   }
 
-  // ---- results: lane (half, l32) holds, for query row c * 32 + l32 of its 64-row block,
-  // dims 32 db + 8 g + 4 half + 0..3 in oacc[db][c][4 g .. 4 g + 3]
+  // ---- results: lane (half, l32) holds, for query row row0 + l32, dims
+  // 32 db + 8 g + 4 half + 0..3 in oacc[db][4 g .. 4 g + 3]
   if (p.splits == 1) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int r = row0 + c * 32 + l32;
-      if (r >= p.rows) continue;
-      const int u = r / p.group, h = kvh * p.group + r % p.group;
-      bf16* o = static_cast<bf16*>(a.out) + ((int64_t(b) * N + u) * a.Hq + h) * kD + 4 * half;
-      const float inv = 1.0f / lsum[c];
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16& v = oacc[db][c];
-          const bf16x4 ov = {static_cast<bf16>(v[4 * g] * inv), static_cast<bf16>(v[4 * g + 1] * inv),
-                             static_cast<bf16>(v[4 * g + 2] * inv), static_cast<bf16>(v[4 * g + 3] * inv)};
-          *reinterpret_cast<bf16x4*>(o + 32 * db + 8 * g) = ov;
-        }
-    }
-    return;
-  }
-  const int64_t slot0 = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave;
-  float2* ml = static_cast<float2*>(a.workspace) + slot0;
-  float* po = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot0 * kD;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int q = c * 32 + l32;
-    if (half == 0) ml[q] = make_float2(m_run[c], lsum[c]);
+    if (!live) return;
+    bf16* o = static_cast<bf16*>(a.out) + ((int64_t(b) * N + u_q) * a.Hq + h_q) * kD + 4 * half;
+    const float inv = 1.0f / lsum;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x16& v = oacc[db][c];
-        *reinterpret_cast<float4*>(po + q * kD + 32 * db + 8 * g + 4 * half) =
-            make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+        const f32x16& v = oacc[db];
+        const bf16x4 ov = {static_cast<bf16>(v[4 * g] * inv), static_cast<bf16>(v[4 * g + 1] * inv),
+                           static_cast<bf16>(v[4 * g + 2] * inv), static_cast<bf16>(v[4 * g + 3] * inv)};
+        *reinterpret_cast<bf16x4*>(o + 32 * db + 8 * g) = ov;
       }
+    return;
   }
+  const int64_t slot = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave + l32;
+  if (half == 0) static_cast<float2*>(a.workspace)[slot] = make_float2(m_run, lsum);
+  float* po = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kD + 4 * half;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x16& v = oacc[db];
+      *reinterpret_cast<float4*>(po + 32 * db + 8 * g) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+    }
 }
 
-// Merge of the splits: thread (row, 4 dims) combines the splits' (m, l, O) partials.
+// Merge of the splits: thread (row, 4 dims) combines the splits' (m, l, O) partials.  The
+// splits are visited eight at a time with every load of a group issued before any is used,
+// so that a thread waits for memory once per group rather than once per split.
+constexpr int kMergeGroup = 8;
+
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   if (round_failed(p.status)) return;
   const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -643,20 +716,38 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   const int row = qb * p.qrows + r;
   if (row >= p.rows) return;
   const int64_t base = uq * p.splits * p.qrows + r;  // slot of split 0
-  float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.ml[base + int64_t(s) * p.qrows].x);
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < p.splits; ++s) {
-    const int64_t slot = base + int64_t(s) * p.qrows;
-    const float2 ml = p.ml[slot];
-    const float wt = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - M);
-    L += wt * ml.y;
-    const float4 v = *reinterpret_cast<const float4*>(p.o + slot * kD + 4 * d4);
-    acc.x += wt * v.x;
-    acc.y += wt * v.y;
-    acc.z += wt * v.z;
-    acc.w += wt * v.w;
+  for (int s0 = 0; s0 < p.splits; s0 += kMergeGroup) {
+    float2 ml[kMergeGroup];
+    float4 v[kMergeGroup];
+#pragma unroll
+    for (int k = 0; k < kMergeGroup; ++k) {  // slots past the last split re-read split 0
+      const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
+      ml[k] = p.ml[slot];
+      v[k] = *reinterpret_cast<const float4*>(p.o + slot * kD + 4 * d4);
+    }
+    float Mg = M;
+#pragma unroll
+    for (int k = 0; k < kMergeGroup; ++k)
+      if (s0 + k < p.splits) Mg = fmaxf(Mg, ml[k].x);
+    // rescale what the earlier groups accumulated, then add this group
+    const float c = M == -INFINITY ? 0.f : exp2_fast(M - Mg);
+    L *= c;
+    acc.x *= c;
+    acc.y *= c;
+    acc.z *= c;
+    acc.w *= c;
+#pragma unroll
+    for (int k = 0; k < kMergeGroup; ++k) {
+      const float wt = (s0 + k < p.splits && ml[k].x != -INFINITY) ? exp2_fast(ml[k].x - Mg) : 0.f;
+      L += wt * ml[k].y;
+      acc.x += wt * v[k].x;
+      acc.y += wt * v[k].y;
+      acc.z += wt * v[k].z;
+      acc.w += wt * v[k].w;
+    }
+    M = Mg;
   }
   const float inv = 1.0f / L;
   const int b = unit / p.Hkv, kvh = unit % p.Hkv;
@@ -695,8 +786,8 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   for (int j = 0; j < kD / 2; ++j) p.theta[j] = std::pow(a.rope_base, -2.0 * j / kD);
   const unsigned grid = unsigned(int64_t(plan.units) * plan.splits * plan.qblocks);
   const void* attn = reinterpret_cast<const void*>(&tree_attn_mfma_kernel);
-  if (plan.splits == 1) return launch(attn, dim3(grid), dim3(256), 0, stream, p, ev_start, ev_stop);
-  const medusa_status st = launch(attn, dim3(grid), dim3(256), 0, stream, p, ev_start, nullptr);
+  if (plan.splits == 1) return launch(attn, dim3(grid), dim3(kThreads), 0, stream, p, ev_start, ev_stop);
+  const medusa_status st = launch(attn, dim3(grid), dim3(kThreads), 0, stream, p, ev_start, nullptr);
   if (st != MEDUSA_OK) return st;
   MergeArgs m{};
   m.ml = static_cast<const float2*>(a.workspace);
