@@ -117,9 +117,8 @@ def build_sets(w, x, tree, n_sets, torch, M):
              "kc": dev(x["k_cache"], dt), "vc": dev(x["v_cache"], dt),
              "logits": dev(x["logits"]) if x["logits"] is not None else None,
              "tids": dev(x["target_ids"]) if x["target_ids"] is not None else None,
-             "cand": dev(x["candidates"]), "ctl": pristine.clone()}
+             "cand": dev(x["candidates"])}
         s["out"] = torch.empty_like(s["q"])
-        s["prefix"], s["status"] = s["ctl"][: w.B], s["ctl"][w.B:]
         s["attn_ws"] = torch.zeros(max(attn_ws, 16), dtype=torch.uint8, device="cuda")
         s["acc_ws"] = torch.zeros(acc_ws, dtype=torch.uint8, device="cuda")
         s["best"] = torch.zeros(w.B, dtype=torch.int32, device="cuda")
@@ -222,31 +221,37 @@ def main():
     width = tree["path_width"]
     p = lambda t: None if t is None else t.data_ptr()
 
-    # argument tuples built once per set: the timed loop only calls into the library
+    # Every step gets its own control block (prefix lengths P_b, then the status word),
+    # filled with the round's initial values before timing: compaction advances P_b by the
+    # accepted count, and a fresh block per step keeps every step at the same P without a
+    # reset copy inside the timed loop.  Argument tuples are built up front as well, so the
+    # timed loop only calls into the library.
+    total = args.warmup + args.steps
+    ctl = pristine.repeat(total, 1).contiguous()   # [steps][B + 1]
+    kc_arrs = [(ctypes.c_void_p * 1)(s["kc"].data_ptr()) for s in sets]
+    vc_arrs = [(ctypes.c_void_p * 1)(s["vc"].data_ptr()) for s in sets]
     calls = []
-    for s in sets:
-        kc_arr = (ctypes.c_void_p * 1)(s["kc"].data_ptr())
-        vc_arr = (ctypes.c_void_p * 1)(s["vc"].data_ptr())
+    for i in range(total):
+        s, kc_arr, vc_arr = sets[i % n_sets], kc_arrs[i % n_sets], vc_arrs[i % n_sets]
+        prefix, status = p(ctl[i]), p(ctl[i, w.B:])
         attn = [sptr, dcode, w.B, w.Hq, w.Hkv, w.d, N, p(shared["depth"]), p(shared["mask"]),
-                tree["mask_words"], p(s["prefix"]), p(s["q"]), p(s["kn"]), p(s["vn"]), p(s["kc"]),
+                tree["mask_words"], prefix, p(s["q"]), p(s["kn"]), p(s["vn"]), p(s["kc"]),
                 p(s["vc"]), x["S_max"], float(w.rope_base), p(s["out"]), p(s["attn_ws"]),
-                s["attn_ws"].numel(), p(s["status"])]
+                s["attn_ws"].numel(), status]
         acc = (sptr, w.B, N, w.vocab if x["logits"] is not None else 0, p(s["logits"]), p(s["tids"]),
                p(s["cand"]), x["candidates"].shape[1], p(shared["tidx"]), p(shared["retrieve"]), nn,
                width, p(s["best"]), p(s["alen"]), p(s["tokens"]), p(s["frontier"]), p(s["acc_ws"]),
-               s["acc_ws"].numel(), p(s["status"]), None, None)
+               s["acc_ws"].numel(), status, None, None)
         cmp_ = (sptr, dcode, 1, w.B, w.Hkv, w.d, x["S_max"], N, ctypes.cast(kc_arr, ctypes.c_void_p),
                 ctypes.cast(vc_arr, ctypes.c_void_p), p(shared["retrieve"]), nn, width, p(s["best"]),
-                p(s["alen"]), p(s["prefix"]), p(s["status"]), None, None)
-        calls.append((s, attn, acc, cmp_, kc_arr, vc_arr))
+                p(s["alen"]), prefix, status, None, None)
+        calls.append((attn, acc, cmp_))
 
     ev = HipEvents()
-    total = args.warmup + args.steps
     events = [(ev.create(), ev.create()) for _ in range(total)]
 
     def step(i):
-        s, attn, acc, cmp_, _, _ = calls[i % n_sets]
-        s["ctl"].copy_(pristine)
+        attn, acc, cmp_ = calls[i]
         rc = lib.medusa_tree_attn(*attn, events[i][0], events[i][1])
         rc |= lib.medusa_accept(*acc)
         rc |= lib.medusa_kv_compact(*cmp_)
@@ -262,9 +267,9 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
 
-    statuses = [int(s["status"].item()) for s in sets]
-    if any(statuses):
-        raise RuntimeError(f"device status words {statuses}: the round failed")
+    statuses = ctl[:, w.B].cpu().numpy()
+    if statuses.any():
+        raise RuntimeError(f"device status words {sorted(set(statuses.tolist()))}: the round failed")
     attn_ms = np.array([ev.elapsed_ms(a, b) for a, b in events[args.warmup:]])
     for a, b in events:
         ev.destroy(a)

@@ -10,7 +10,8 @@
 // "Medusa Part II: Candidate Trees, Verification, and Acceptance", Part 7:
 //   the same cumulative-product rule; padded slots are path ends, not tokens.
 //
-// Kernel 1 (argmax): one block per (sequence, row) streams the V logits once.
+// Kernel 1 (argmax): one block per (sequence, row) streams the V logits once,
+//                    eight 16-byte loads in flight per thread.
 // Kernel 2 (select):  one block per sequence counts each path's matching
 //                     prefix and picks the first longest.
 
@@ -42,31 +43,47 @@ __device__ __forceinline__ void keep_better(float& v, int& i, float ov, int oi) 
   }
 }
 
-__global__ __launch_bounds__(256) void argmax_kernel(AcceptArgs a) {
+constexpr int kArgmaxThreads = 512;
+constexpr int kArgmaxUnroll = 8;  // 16-byte loads each thread has in flight
+
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(AcceptArgs a) {
   if (round_failed(a.status)) return;
   const int64_t r = blockIdx.x;
   const float* row = a.logits + r * a.V;
   float best = -INFINITY;
   int idx = INT_MAX;
   bool nan = false;
+  auto take = [&](float e, int i) __attribute__((always_inline)) {
+    nan = nan || (e != e);
+    if (e == e) keep_better(best, idx, e, i);
+  };
   const bool vec = (a.V % 4 == 0) && ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
   if (vec) {
+    // kArgmaxUnroll loads per thread are issued before any is compared, so that a row is
+    // streamed with about 64 KiB in flight per workgroup; loads past the row end read
+    // element 0 again (in bounds) and are not compared
     const float4* row4 = reinterpret_cast<const float4*>(row);
-    for (int c = threadIdx.x; c < a.V / 4; c += blockDim.x) {
-      const float4 x = row4[c];
-      const float e[4] = {x.x, x.y, x.z, x.w};
+    const int n4 = a.V / 4;
+    for (int c0 = threadIdx.x; c0 < n4; c0 += kArgmaxThreads * kArgmaxUnroll) {
+      float4 x[kArgmaxUnroll];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        nan = nan || (e[j] != e[j]);
-        if (e[j] == e[j]) keep_better(best, idx, e[j], 4 * c + j);
+      for (int k = 0; k < kArgmaxUnroll; ++k) {
+        const int c = c0 + k * kArgmaxThreads;
+        x[k] = row4[c < n4 ? c : 0];
+      }
+#pragma unroll
+      for (int k = 0; k < kArgmaxUnroll; ++k) {
+        const int c = c0 + k * kArgmaxThreads;
+        if (c < n4) {
+          take(x[k].x, 4 * c);
+          take(x[k].y, 4 * c + 1);
+          take(x[k].z, 4 * c + 2);
+          take(x[k].w, 4 * c + 3);
+        }
       }
     }
   } else {
-    for (int i = threadIdx.x; i < a.V; i += blockDim.x) {
-      const float e = row[i];
-      nan = nan || (e != e);
-      if (e == e) keep_better(best, idx, e, i);
-    }
+    for (int i = threadIdx.x; i < a.V; i += kArgmaxThreads) take(row[i], i);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -74,8 +91,9 @@ __global__ __launch_bounds__(256) void argmax_kernel(AcceptArgs a) {
     const int oi = __shfl_xor(idx, off, 64);
     keep_better(best, idx, ov, oi);
   }
-  __shared__ float wv[4];
-  __shared__ int wi[4];
+  constexpr int kWaves = kArgmaxThreads / 64;
+  __shared__ float wv[kWaves];
+  __shared__ int wi[kWaves];
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   if (lane == 0) {
     wv[wave] = best;
@@ -87,7 +105,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(AcceptArgs a) {
       raise_status(a.status, MEDUSA_EINVAL);
       return;
     }
-    for (int w = 1; w < int(blockDim.x / 64); ++w) keep_better(wv[0], wi[0], wv[w], wi[w]);
+    for (int w = 1; w < kWaves; ++w) keep_better(wv[0], wi[0], wv[w], wi[w]);
     a.target[r] = wi[0];
   }
 }
@@ -223,7 +241,7 @@ extern "C" medusa_status medusa_accept(void* stream, int32_t B, int32_t N, int32
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (logits != nullptr) {
     medusa_status st = launch(reinterpret_cast<const void*>(&argmax_kernel),
-                              dim3(unsigned(int64_t(B) * N)), dim3(256), 0, s, a, ev_start, nullptr);
+                              dim3(unsigned(int64_t(B) * N)), dim3(kArgmaxThreads), 0, s, a, ev_start, nullptr);
     if (st != MEDUSA_OK) return st;
     ev_start = nullptr;
   }

@@ -62,6 +62,9 @@ constexpr int kD = 128;          // head dimension
 constexpr int kTile = 32;        // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kKeyPhases = kWaves / 4;   // wavefronts per SIMD: each takes every kKeyPhases-th tile
+constexpr int kDmaRows = 32 / kWaves;     // rows of every tile each wavefront loads
+constexpr int kDmaOps = kDmaRows / 4;     // direct-to-LDS instructions per matrix and tile
 constexpr int kRowsWave = 32;    // query rows per wavefront
 constexpr int kRing = 8;         // tile buffers in LDS
 constexpr int kTileBytes = 2 * kTile * kD * 2;  // K then V of one tile
@@ -113,7 +116,7 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
   p.units = B * Hkv;
   p.group = Hq / Hkv;
   p.rows = N * p.group;
-  p.n_kp = 2;
+  p.n_kp = kKeyPhases;
   p.qrows = kRowsWave * kWaves / p.n_kp;
   p.qblocks = (p.rows + p.qrows - 1) / p.qrows;
   const int32_t wgs = p.units * p.qblocks;
@@ -173,9 +176,17 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 }
 
 // wait until at most n of this wavefront's vector memory operations are outstanding
-// (n rounded down to an even count, which only makes the wait stricter)
+// (n rounded down to an even count and capped at 30, which only makes the wait stricter)
 __device__ __forceinline__ void wait_vm(int n) {
-  switch (n >= 14 ? 7 : n >> 1) {
+  switch (n >= 30 ? 15 : n >> 1) {
+    case 15: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt vmcnt(26)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(22)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
     case 7: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
     case 6: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
     case 5: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
@@ -267,30 +278,45 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     return s_ring[(i & (S - 1)) * n_kp + k];
   };
 
-  // Rows 4 w .. 4 w + 3 of one tile's K and V by direct global->LDS loads (wavefront w,
-  // one instruction per matrix): lane l lands at byte 1024 w + 16 l of the matrix, i.e.
-  // row 4 w + l / 16, stored chunk l % 16, and fetches logical chunk (l % 16) ^ key(row),
-  // so that the buffer holds the layout swz() reads back.
-  const int rt_dma = 4 * wave + (lane >> 4);
-  const int chunk_dma = (lane & 15) ^ swz_key(rt_dma);  // logical chunk this lane fetches
-  const uint32_t poff = uint32_t(rt_dma * 256 + (chunk_dma << 4));
+  // Rows kDmaRows w .. kDmaRows (w + 1) - 1 of one tile's K and V by direct global->LDS
+  // loads (wavefront w, kDmaOps instructions of four rows per matrix): in instruction h,
+  // lane l lands at byte 256 kDmaRows w + 1024 h + 16 l of the matrix, i.e. row
+  // kDmaRows w + 4 h + l / 16, stored chunk l % 16, and fetches logical chunk
+  // (l % 16) ^ key(row), so that the buffer holds the layout swz() reads back.
+  int rt_dma[kDmaOps], chunk_dma[kDmaOps];
+  uint32_t poff[kDmaOps];
+#pragma unroll
+  for (int h = 0; h < kDmaOps; ++h) {
+    rt_dma[h] = kDmaRows * wave + 4 * h + (lane >> 4);
+    chunk_dma[h] = (lane & 15) ^ swz_key(rt_dma[h]);  // logical chunk this lane fetches
+    poff[h] = uint32_t(rt_dma[h] * 256 + (chunk_dma[h] << 4));
+  }
   auto issue_tile = [&](int t, unsigned char* buf) __attribute__((always_inline)) {
-    const uint32_t lds = lds_addr(buf) + 1024 * wave;
+    const uint32_t lds = lds_addr(buf) + 256 * kDmaRows * wave;
     if ((t + 1) * kTile <= P) {  // full prefix tile
       const int64_t off = int64_t(t) * kTile * kD;
-      dma16(kc + off, poff, lds);
-      dma16(vc + off, poff, lds + 8192);
+#pragma unroll
+      for (int h = 0; h < kDmaOps; ++h) {
+        dma16(kc + off, poff[h], lds + 1024 * h);
+        dma16(vc + off, poff[h], lds + 8192 + 1024 * h);
+      }
     } else if (t < n_pre) {  // the partial prefix tile: rows past P repeat row 0
       const int64_t off = int64_t(t) * kTile * kD;
-      const int r = t * kTile + rt_dma < P ? rt_dma : 0;
-      const uint32_t o = uint32_t(r * 256 + (chunk_dma << 4));
-      dma16(kc + off, o, lds);
-      dma16(vc + off, o, lds + 8192);
+#pragma unroll
+      for (int h = 0; h < kDmaOps; ++h) {
+        const int r = t * kTile + rt_dma[h] < P ? rt_dma[h] : 0;
+        const uint32_t o = uint32_t(r * 256 + (chunk_dma[h] << 4));
+        dma16(kc + off, o, lds + 1024 * h);
+        dma16(vc + off, o, lds + 8192 + 1024 * h);
+      }
     } else {  // staged rows from k_new / v_new; rows past the tree repeat node 0
-      const int u = (t - n_pre) * kTile + rt_dma;
-      const uint32_t o = uint32_t(((u < N ? u : 0) * a.Hkv * kD + 8 * chunk_dma) * 2);
-      dma16(kn, o, lds);
-      dma16(vn, o, lds + 8192);
+#pragma unroll
+      for (int h = 0; h < kDmaOps; ++h) {
+        const int u = (t - n_pre) * kTile + rt_dma[h];
+        const uint32_t o = uint32_t(((u < N ? u : 0) * a.Hkv * kD + 8 * chunk_dma[h]) * 2);
+        dma16(kn, o, lds + 1024 * h);
+        dma16(vn, o, lds + 8192 + 1024 * h);
+      }
     }
   };
   auto issue_stage = [&](int i) __attribute__((always_inline)) {
@@ -300,9 +326,15 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     }
   };
   // wait until this wavefront's loads of stage i have landed, stages up to `last` having
-  // been issued (two loads per tile)
+  // been issued (2 kDmaOps loads per tile).  In the steady state of the ring that is always
+  // the same count, tested first so that the common case costs one compare.
+  constexpr int kSteadyWait = 2 * kDmaOps * kKeyPhases * (kRing / kKeyPhases - 3);
   auto wait_stage = [&](int i, int last) __attribute__((always_inline)) {
-    wait_vm(last > i ? 2 * (tile_end(last) - tile_end(i)) : 0);
+    const int n = last > i ? 2 * kDmaOps * (tile_end(last) - tile_end(i)) : 0;
+    if (n == kSteadyWait)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteadyWait) : "memory");
+    else
+      wait_vm(n);
   };
 
   // The first stage's tile loads need only P (a scalar load): issue them now, while the
@@ -400,14 +432,15 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     }
   }
 
-  // Staged rows of one tile that this wavefront loaded (rows 4 w .. 4 w + 3): rotate K in
+  // Staged rows of one tile that this wavefront loaded (rows kDmaRows w ..): rotate K in
   // place to P + depth(u); query block 0 also stores K~ and V to cache rows P + u.  Lane
-  // l < 32 takes row 4 w + l / 8 and the chunk pair (l % 8, l % 8 + 8), i.e. dims j, j + 64.
+  // l < 8 kDmaRows takes row kDmaRows w + l / 8 and the chunk pair (l % 8, l % 8 + 8),
+  // i.e. dims j and j + 64.
   // Depths come from the LDS copy; trees too large for it read them from memory, in a
   // separate instantiation so that the common path carries no wait for that load.
   auto fix_staged = [&](int t, unsigned char* buf, auto depth_in_memory) __attribute__((always_inline)) {
-    if (lane >= 32) return;
-    const int rt = 4 * wave + (lane >> 3), c = lane & 7;
+    if (lane >= 8 * kDmaRows) return;
+    const int rt = kDmaRows * wave + (lane >> 3), c = lane & 7;
     const int uu = (t - n_pre) * kTile + rt;
     const int u = uu < N ? uu : 0;
     const int dep = decltype(depth_in_memory)::value ? a.depth[u] : int(s_dep[u]);
