@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5, l32 = lane & 31;
-  const int n_kp = p.n_kp;
+  constexpr int n_kp = kKeyPhases;
   const int kp = wave % n_kp, rb = wave / n_kp;  // key phase, 32-row block
 
   // ---- this workgroup's (sequence, kv head, split, query block)
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int n_stages = (T + n_kp - 1) / n_kp;
   const int s_lo = int(int64_t(split) * n_stages / p.splits);
   const int n_st = int(int64_t(split + 1) * n_stages / p.splits) - s_lo;
-  const int S = kRing / n_kp;  // 8 or 4 stages in the ring
+  constexpr int S = kRing / n_kp;  // stages in the ring
   auto tile_start = [&](int i) __attribute__((always_inline)) { return (s_lo + i) * n_kp; };
   auto tile_end = [&](int i) __attribute__((always_inline)) { return min(T, (s_lo + i + 1) * n_kp); };
 
@@ -665,7 +665,65 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     __syncthreads();
     prep(0, s_cur, b_cur);
   }
-  for (int i = 0; i < n_st; ++i) {
+
+  // Steady state.  Step i is steady when every tile it touches -- those of stages i and
+  // i+1 and those of stage i+S-1, which it issues -- is a full, unmasked prefix tile
+  // (index below n_safe) and the ring is full.  Such steps need no tile classification,
+  // masks, staged-row fixes or variable waits, and their load addresses advance by a fixed
+  // stride, so they run as a separate loop with as few instructions as possible.
+  const int n_safe = min(P / kTile, n_pre - 1);  // tiles below this are full and unmasked
+  const int hot_end = max(0, min(n_st - S + 1, n_safe / n_kp - s_lo - S + 1));
+  int i = 0;
+  if (hot_end > 0) {
+    // global addresses of the tiles of stage S-1 (issued by step 0); lane offsets in poff[]
+    const bf16* kq = kc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
+    const bf16* vq = vc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
+    const uint32_t ring0 = lds_addr(&s_ring[0][0]) + 256 * kDmaRows * wave;
+    auto steady = [&](int j, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteadyWait) : "memory");
+      __syncthreads();  // stage j+1 visible; every wavefront is done with stage j-1
+      const uint32_t dst = ring0 + uint32_t(((j + S - 1) & (S - 1)) * n_kp * kTileBytes);
+#pragma unroll
+      for (int k = 0; k < n_kp; ++k)
+#pragma unroll
+        for (int h = 0; h < kDmaOps; ++h) {
+          dma16(kq + k * kTile * kD, poff[h], dst + k * kTileBytes + 1024 * h);
+          dma16(vq + k * kTile * kD, poff[h], dst + k * kTileBytes + 8192 + 1024 * h);
+        }
+      kq += n_kp * kTile * kD;
+      vq += n_kp * kTile * kD;
+      unsigned char* tn = s_ring[((j + 1) & (S - 1)) * n_kp + kp];
+      unsigned char* tc = s_ring[(j & (S - 1)) * n_kp + kp];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        bf16x8 kop[4];
+        read_k(tn, kh, kop);
+        qk(kh, kop, sn);
+      }
+      const float m_use = update_max(sc);
+      bf16x8 pop[2];
+      probs(sc, m_use, pop);
+#pragma unroll
+      for (int dh = 0; dh < 2; ++dh) {
+        bf16x8 vop[2][2];
+        read_v(tc, dh, vop);
+        pv(dh, vop, pop);
+      }
+    };
+    // unrolled twice so that the two score tiles trade places without copies
+    for (; i + 2 <= hot_end; i += 2) {
+      steady(i, s_cur, s_nxt);
+      steady(i + 1, s_nxt, s_cur);
+    }
+    if (i < hot_end) {
+      steady(i, s_cur, s_nxt);
+      s_cur = s_nxt;
+      ++i;
+    }
+    b_cur = 0xffffffffu;  // the current tile is a full prefix tile
+  }
+  // the remaining steps: the end of the ring, partial and staged tiles
+  for (; i < n_st; ++i) {
     step(i, s_cur, b_cur, s_nxt, b_nxt);
     s_cur = s_nxt;
     b_cur = b_nxt;
