@@ -169,9 +169,10 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
   const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(addr)));
   const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(addr >> 32)));
   const uint64_t sbase = uint64_t(lo) | (uint64_t(hi) << 32);
+  const uint32_t m0v = uint32_t(__builtin_amdgcn_readfirstlane(lds));
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds), "v"(voff), "s"(sbase)
+               : "s"(m0v), "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
 
@@ -196,6 +197,18 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 1: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
+}
+
+// maxima without the canonicalising moves IEEE-mode fmaxf adds in front of MFMA results
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // an empty use of a register, so that the compiler completes the load producing it here
@@ -675,6 +688,17 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int hot_end = max(0, min(n_st - S + 1, n_safe / n_kp - s_lo - S + 1));
   int i = 0;
   if (hot_end > 0) {
+    // In the steady loop the score tiles are kept relative to the running maximum: the
+    // first score MFMA of a tile starts from the accumulator value -m_run, so exp2 takes
+    // the accumulator directly.  The running maximum is checked at the end of each step,
+    // on the scores just formed, and moved (rarely) before they are used.
+    update_max(s_cur);
+    f32x16 negm;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s_cur[e] -= m_run;
+      negm[e] = -m_run;
+    }
     // global addresses of the tiles of stage S-1 (issued by step 0); lane offsets in poff[]
     const bf16* kq = kc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
     const bf16* vq = vc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
@@ -692,22 +716,50 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
         }
       kq += n_kp * kTile * kD;
       vq += n_kp * kTile * kD;
-      unsigned char* tn = s_ring[((j + 1) & (S - 1)) * n_kp + kp];
-      unsigned char* tc = s_ring[(j & (S - 1)) * n_kp + kp];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        bf16x8 kop[4];
-        read_k(tn, kh, kop);
-        qk(kh, kop, sn);
-      }
-      const float m_use = update_max(sc);
+      const unsigned char* tn = s_ring[((j + 1) & (S - 1)) * n_kp + kp];
+      const unsigned char* tc = s_ring[(j & (S - 1)) * n_kp + kp];
+      // every operand read of the step is issued up front
+      bf16x8 kop[2][4], vop[2][2][2];
+      read_k(tn, 0, kop[0]);
+      read_k(tn, 1, kop[1]);
+      read_v(tc, 0, vop[0]);
+      read_v(tc, 1, vop[1]);
+      // probabilities of tile j against the running maximum
       bf16x8 pop[2];
-      probs(sc, m_use, pop);
+      probs(sc, 0.f, pop);
+      // scores of tile j+1, relative to the running maximum
 #pragma unroll
-      for (int dh = 0; dh < 2; ++dh) {
-        bf16x8 vop[2][2];
-        read_v(tc, dh, vop);
-        pv(dh, vop, pop);
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kh][jj], qop[4 * kh + jj], kh == 0 && jj == 0 ? negm : sn, 0, 0, 0);
+      pv(0, vop[0], pop);
+      pv(1, vop[1], pop);
+      // maximum of tile j+1; the reference moves when it exceeds the slack
+      float x0 = max3f(sn[0], sn[1], sn[2]), x1 = max3f(sn[3], sn[4], sn[5]);
+      float x2 = max3f(sn[6], sn[7], sn[8]), x3 = max3f(sn[9], sn[10], sn[11]);
+      float x4 = max3f(sn[12], sn[13], sn[14]);
+      x0 = max3f(x0, x1, x2);
+      x3 = max3f(x3, x4, sn[15]);
+      x0 = max2f(x0, x3);
+      float y0, y1;
+      halves(x0, y0, y1);
+      const float tmax = max2f(y0, y1);
+      const bool grow = tmax > kRescaleSlack;
+      if (__ballot(grow)) {
+        const float shift = grow ? tmax : 0.f;
+        const float corr = exp2_fast(-shift);
+        l_run *= corr;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
+        m_run += shift;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sn[e] -= shift;
+          negm[e] = -m_run;
+        }
       }
     };
     // unrolled twice so that the two score tiles trade places without copies
@@ -720,6 +772,9 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       s_cur = s_nxt;
       ++i;
     }
+    // back to absolute scores for the general steps
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s_cur[e] += m_run;
     b_cur = 0xffffffffu;  // the current tile is a full prefix tile
   }
   // the remaining steps: the end of the ring, partial and staged tiles
