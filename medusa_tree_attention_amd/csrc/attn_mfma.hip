@@ -94,7 +94,7 @@ struct MfmaArgs {
   int32_t splits;    // workgroups sharing one query block's keys
   int32_t xcd_map;   // keep the query blocks of one (unit, split) on one XCD
   int64_t o_offset;  // byte offset of the partial O in the workspace
-  double theta[kD / 2];  // RoPE inverse frequencies base^(-2i/d)
+  double log2_base;  // log2 of the RoPE base: frequency i is 2^(-(2i/d) log2 base)
 };
 
 struct MergeArgs {
@@ -260,7 +260,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   for (int s = 0; s < 8; ++s) raw[s] = *reinterpret_cast<const uint4*>(qr + 16 * s + 8 * half);
   const int dep_q = a.depth[u_q];
   const int dep0 = a.depth[min(tid, N - 1)];
-  const double theta = p.theta[tid % (kD / 2)];  // the frequency of this thread's phase entries
   // visibility of staged tile k (nodes 32 k .. 32 k + 31) for this lane's query node
   uint64_t mword[kMaskLds / 2];
 #pragma unroll
@@ -273,8 +272,14 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int n_pre = (P + kTile - 1) / kTile;
   const int T = n_pre + n_stg;
   const int n_stages = (T + n_kp - 1) / n_kp;
-  const int s_lo = int(int64_t(split) * n_stages / p.splits);
-  const int n_st = int(int64_t(split + 1) * n_stages / p.splits) - s_lo;
+  // Split boundaries: stages holding a partial or staged tile (masks, staged-row fixes, the
+  // general path) count twice, so the last split, which holds them, gets fewer stages.
+  const int n_heavy = n_stages - (P / kTile) / n_kp;
+  auto bound = [&](int k) __attribute__((always_inline)) {
+    return k == p.splits ? n_stages : min(n_stages, int(int64_t(k) * (n_stages + n_heavy) / p.splits));
+  };
+  const int s_lo = bound(split);
+  const int n_st = bound(split + 1) - s_lo;
   constexpr int S = kRing / n_kp;  // stages in the ring
   auto tile_start = [&](int i) __attribute__((always_inline)) { return (s_lo + i) * n_kp; };
   auto tile_end = [&](int i) __attribute__((always_inline)) { return min(T, (s_lo + i + 1) * n_kp); };
@@ -355,6 +360,21 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // sequence below, which then raises the error).
   if (P >= 0 && P <= a.S_max - N && n_st > 0) issue_stage(0);
 
+  // ---- RoPE phases (cos, sin) of positions P + d for every depth d < 32: the angle is
+  // formed and reduced modulo 2 pi in binary64, then evaluated in fp32.  Thread tid fills
+  // entries (d, tid % 64) for d = tid / 64 + 8 k.  This needs only P, so it runs while
+  // the set-up loads and the first stage's tiles are in flight.
+  static_assert(kThreads % (kD / 2) == 0, "a thread's phase entries share one frequency");
+  const double theta = exp2(-double(tid % (kD / 2)) * (2.0 / kD) * p.log2_base);
+  for (int i = tid; i < kTableDepth * (kD / 2); i += kThreads) {
+    const int d = i / (kD / 2), j = i % (kD / 2);
+    const double x = double(P + d) * theta;
+    const double k = rint(x * kInvTwoPi);
+    const float r = float(fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, x)));
+    float sn, cs;
+    sincosf(r, &sn, &cs);
+    s_cs[d][j] = make_float2(cs, sn);
+  }
   // consume them all; the first stage's tile loads, issued above, complete with them, so
   // that no tile load is in flight at the early exits below
 #pragma unroll
@@ -371,8 +391,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   }
   touch(uint32_t(dep_q));
   touch(uint32_t(dep0));
-  touch(uint32_t(__double_as_longlong(theta)));
-  touch(uint32_t(__double_as_longlong(theta) >> 32));
   touch(uint32_t(P_lane));
   wait_vm(0);
   if (failed) return;
@@ -403,19 +421,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int first = min(S - 1, n_st);
   for (int i = 1; i < first; ++i) issue_stage(i);
 
-  // ---- RoPE phases (cos, sin) of positions P + d for every depth d < 32: the angle is
-  // formed and reduced modulo 2 pi in binary64, then evaluated in fp32.  Thread tid
-  // fills entries (d, tid % 64) for d = tid / 64 + 8 k.
-  static_assert(kThreads % (kD / 2) == 0, "a thread's phase entries share one frequency");
-  for (int i = tid; i < kTableDepth * (kD / 2); i += kThreads) {
-    const int d = i / (kD / 2), j = i % (kD / 2);
-    const double x = double(P + d) * theta;
-    const double k = rint(x * kInvTwoPi);
-    const float r = float(fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, x)));
-    float sn, cs;
-    sincosf(r, &sn, &cs);
-    s_cs[d][j] = make_float2(cs, sn);
-  }
   if (lane == 0) s_bad[wave] = 0;
   if (__ballot(bad) != 0 && lane == 0) s_bad[wave] = 1;
   __syncthreads();
@@ -680,12 +685,12 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   }
 
   // Steady state.  Step i is steady when every tile it touches -- those of stages i and
-  // i+1 and those of stage i+S-1, which it issues -- is a full, unmasked prefix tile
-  // (index below n_safe) and the ring is full.  Such steps need no tile classification,
-  // masks, staged-row fixes or variable waits, and their load addresses advance by a fixed
-  // stride, so they run as a separate loop with as few instructions as possible.
-  const int n_safe = min(P / kTile, n_pre - 1);  // tiles below this are full and unmasked
-  const int hot_end = max(0, min(n_st - S + 1, n_safe / n_kp - s_lo - S + 1));
+  // i+1 and those of stage i+S-1, which it issues -- is a full prefix tile (index below
+  // P / kTile) and the ring is full.  Such steps need no tile classification, masks,
+  // staged-row fixes or variable waits, and their load addresses advance by a fixed
+  // stride, so they run as a separate loop with as few instructions as possible.  The
+  // remaining steps (the ring's drain, partial and staged tiles) take the general path.
+  const int hot_end = max(0, min(n_st - S + 1, (P / kTile) / n_kp - s_lo - S + 1));
   int i = 0;
   if (hot_end > 0) {
     // In the steady loop the score tiles are kept relative to the running maximum: the
@@ -929,7 +934,7 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   p.splits = plan.splits;
   p.xcd_map = plan.xcd_map ? 1 : 0;
   p.o_offset = int64_t(plan.o_offset);
-  for (int j = 0; j < kD / 2; ++j) p.theta[j] = std::pow(a.rope_base, -2.0 * j / kD);
+  p.log2_base = std::log2(a.rope_base);
   const unsigned grid = unsigned(int64_t(plan.units) * plan.splits * plan.qblocks);
   const void* attn = reinterpret_cast<const void*>(&tree_attn_mfma_kernel);
   if (plan.splits == 1) return launch(attn, dim3(grid), dim3(kThreads), 0, stream, p, ev_start, ev_stop);
