@@ -99,7 +99,7 @@ struct MfmaArgs {
 
 struct MergeArgs {
   const float2* ml;  // [units][qblocks][splits][qrows] (m, l)
-  const float* o;    // [units][qblocks][splits][qrows][D]
+  const bf16* o;     // [units][qblocks][splits][qrows][D], O / l of the split
   void* out;
   const int32_t* status;
   int32_t Hq, Hkv, N, group, rows, qrows, qblocks, splits;
@@ -129,7 +129,7 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
   p.xcd_map = p.qblocks > 1 && (int64_t(p.units) * p.splits) % 8 == 0;
   const size_t slots = size_t(p.units) * p.qblocks * p.splits * p.qrows;
   p.o_offset = (slots * sizeof(float2) + 255) / 256 * 256;
-  p.bytes = p.splits > 1 ? p.o_offset + slots * kD * sizeof(float) : 256;
+  p.bytes = p.splits > 1 ? p.o_offset + slots * kD * sizeof(bf16) : 256;
   return p;
 }
 
@@ -838,28 +838,34 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       }
     return;
   }
+  // partial of a split: (m, l) in fp32 and O / l rounded to bf16 (zero for a split that saw
+  // no key of the row)
   const int64_t slot = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave + l32;
   if (half == 0) static_cast<float2*>(a.workspace)[slot] = make_float2(m_run, lsum);
-  float* po = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kD + 4 * half;
+  bf16* po = reinterpret_cast<bf16*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kD + 4 * half;
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x16& v = oacc[db];
-      *reinterpret_cast<float4*>(po + 32 * db + 8 * g) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+      const bf16x4 ov = {static_cast<bf16>(v[4 * g] * inv), static_cast<bf16>(v[4 * g + 1] * inv),
+                         static_cast<bf16>(v[4 * g + 2] * inv), static_cast<bf16>(v[4 * g + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * g) = ov;
     }
 }
 
-// Merge of the splits: thread (row, 4 dims) combines the splits' (m, l, O) partials.  The
-// splits are visited eight at a time with every load of a group issued before any is used,
-// so that a thread waits for memory once per group rather than once per split.
+// Merge of the splits: thread (row, 8 dims) combines the splits' partials, weighting split
+// s by l_s 2^(m_s - M).  The splits are visited eight at a time with every load of a group
+// issued before any is used, so that a thread waits for memory once per group rather than
+// once per split.
 constexpr int kMergeGroup = 8;
 
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   if (round_failed(p.status)) return;
   const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int d4 = int(idx & 31);
-  const int64_t g = idx >> 5;  // (unit, query block, row of the block)
+  const int d8 = int(idx & 15);
+  const int64_t g = idx >> 4;  // (unit, query block, row of the block)
   const int r = int(g % p.qrows);
   const int64_t uq = g / p.qrows;
   const int qb = int(uq % p.qblocks);
@@ -868,15 +874,15 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   if (row >= p.rows) return;
   const int64_t base = uq * p.splits * p.qrows + r;  // slot of split 0
   float M = -INFINITY, L = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < p.splits; s0 += kMergeGroup) {
     float2 ml[kMergeGroup];
-    float4 v[kMergeGroup];
+    uint4 v[kMergeGroup];
 #pragma unroll
     for (int k = 0; k < kMergeGroup; ++k) {  // slots past the last split re-read split 0
       const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
       ml[k] = p.ml[slot];
-      v[k] = *reinterpret_cast<const float4*>(p.o + slot * kD + 4 * d4);
+      v[k] = *reinterpret_cast<const uint4*>(p.o + slot * kD + 8 * d8);
     }
     float Mg = M;
 #pragma unroll
@@ -885,28 +891,26 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
     // rescale what the earlier groups accumulated, then add this group
     const float c = M == -INFINITY ? 0.f : exp2_fast(M - Mg);
     L *= c;
-    acc.x *= c;
-    acc.y *= c;
-    acc.z *= c;
-    acc.w *= c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= c;
 #pragma unroll
     for (int k = 0; k < kMergeGroup; ++k) {
-      const float wt = (s0 + k < p.splits && ml[k].x != -INFINITY) ? exp2_fast(ml[k].x - Mg) : 0.f;
-      L += wt * ml[k].y;
-      acc.x += wt * v[k].x;
-      acc.y += wt * v[k].y;
-      acc.z += wt * v[k].z;
-      acc.w += wt * v[k].w;
+      const float wt = (s0 + k < p.splits && ml[k].x != -INFINITY) ? ml[k].y * exp2_fast(ml[k].x - Mg) : 0.f;
+      const bf16x8 o8 = __builtin_bit_cast(bf16x8, v[k]);
+      L += wt;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wt * float(o8[e]);
     }
     M = Mg;
   }
   const float inv = 1.0f / L;
   const int b = unit / p.Hkv, kvh = unit % p.Hkv;
   const int u = row / p.group, h = kvh * p.group + row % p.group;
-  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kD + 4 * d4;
-  const bf16x4 ov = {static_cast<bf16>(acc.x * inv), static_cast<bf16>(acc.y * inv),
-                     static_cast<bf16>(acc.z * inv), static_cast<bf16>(acc.w * inv)};
-  *reinterpret_cast<bf16x4*>(o) = ov;
+  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kD + 8 * d8;
+  bf16x8 ov;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ov[e] = static_cast<bf16>(acc[e] * inv);
+  *reinterpret_cast<bf16x8*>(o) = ov;
 }
 
 }  // namespace
@@ -942,7 +946,7 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   if (st != MEDUSA_OK) return st;
   MergeArgs m{};
   m.ml = static_cast<const float2*>(a.workspace);
-  m.o = reinterpret_cast<const float*>(static_cast<const unsigned char*>(a.workspace) + plan.o_offset);
+  m.o = reinterpret_cast<const bf16*>(static_cast<const unsigned char*>(a.workspace) + plan.o_offset);
   m.out = a.out;
   m.status = a.status;
   m.Hq = a.Hq;
@@ -953,7 +957,7 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   m.qrows = plan.qrows;
   m.qblocks = plan.qblocks;
   m.splits = plan.splits;
-  const int64_t threads = int64_t(plan.units) * plan.qblocks * plan.qrows * 32;
+  const int64_t threads = int64_t(plan.units) * plan.qblocks * plan.qrows * 16;
   return launch(reinterpret_cast<const void*>(&tree_attn_merge_kernel),
                 dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, m, nullptr, ev_stop);
 }
