@@ -862,7 +862,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
 constexpr int kMergeGroup = 8;
 
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
-  if (round_failed(p.status)) return;
+  const bool failed = round_failed(p.status);  // gates the store only
   const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int d8 = int(idx & 15);
   const int64_t g = idx >> 4;  // (unit, query block, row of the block)
@@ -903,6 +903,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
     }
     M = Mg;
   }
+  if (failed) return;
   const float inv = 1.0f / L;
   const int b = unit / p.Hkv, kvh = unit % p.Hkv;
   const int u = row / p.group, h = kvh * p.group + row % p.group;
