@@ -211,8 +211,36 @@ __device__ __forceinline__ float max2f(float a, float b) {
   return r;
 }
 
-// an empty use of a register, so that the compiler completes the load producing it here
-__device__ __forceinline__ void touch(uint32_t v) { asm volatile("" ::"v"(v)); }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Set-up loads issued as inline assembly: the compiler tracks no completion for them, so
+// none of its own waits -- which would also wait for the tile loads issued after them --
+// stands in front of their uses.  A value may be used only after a wait_vm that covers
+// its load, and after pin(), which keeps the uses from moving above that wait.
+__device__ __forceinline__ u32x4 load_b128(const void* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x2 load_b64(const void* p) {
+  u32x2 v;
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t load_b32(const void* p) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+// the status word, read past the caches like a relaxed system-scope atomic load
+__device__ __forceinline__ uint32_t load_b32_coherent(const void* p) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off sc0 sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
 
 __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   const AttnArgs& a = p.a;
@@ -238,33 +266,33 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int n_stg = (N + kTile - 1) / kTile;
 
   __shared__ __attribute__((aligned(16))) unsigned char s_ring[kRing][kTileBytes];
-  __shared__ float2 s_cs[kTableDepth][kD / 2];
+  __shared__ float2 s_cs[kTableDepth][kD / 2 + 2];  // rows padded: lanes at other depths hit other banks
   __shared__ unsigned char s_dep[kDepthLds];
   __shared__ uint32_t s_mw[kWaves][kMaskLds][kRowsWave];
   __shared__ int s_bad[kWaves];
 
-  // ---- set-up loads, independent of each other and issued together: every address is
-  // clamped into range instead of branching, so that no load waits for another.  This
+  // ---- set-up loads, independent of each other and issued together (as inline assembly,
+  // see load_b128): every address is clamped into range instead of branching.  This
   // lane's query row is row0 + l32 of the unit: node u_q, head h_q.
-  const bool failed = round_failed(a.status);
-  const int64_t P_lane = a.prefix_len[min(lane, a.B - 1)];  // sequences 0..63, checked below
-  const int P = a.prefix_len[b];                             // scalar
+  const int P = a.prefix_len[b];  // scalar
   const int row0 = qb * p.qrows + rb * kRowsWave;
   const int rq = row0 + l32;
   const bool live = rq < p.rows;
   const int u_q = live ? rq / p.group : 0;
   const int h_q = kvh * p.group + (live ? rq % p.group : 0);
   const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t(b) * N + u_q) * a.Hq + h_q) * kD;
-  uint4 raw[8];
+  uint32_t st_word = load_b32_coherent(a.status);
+  u32x4 raw[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) raw[s] = *reinterpret_cast<const uint4*>(qr + 16 * s + 8 * half);
-  const int dep_q = a.depth[u_q];
-  const int dep0 = a.depth[min(tid, N - 1)];
-  // visibility of staged tile k (nodes 32 k .. 32 k + 31) for this lane's query node
-  uint64_t mword[kMaskLds / 2];
+  for (int s = 0; s < 8; ++s) raw[s] = load_b128(qr + 16 * s + 8 * half);
+  uint32_t dep_q_w = load_b32(a.depth + u_q);
+  uint32_t dep0_w = load_b32(a.depth + min(tid, N - 1));
+  uint32_t P_lane_w = load_b32(a.prefix_len + min(lane, a.B - 1));  // sequences 0..63, checked below
+  // visibility of staged tiles 2k and 2k + 1 (nodes 64 k .. 64 k + 63) for this lane's node
+  u32x2 mword[kMaskLds / 2];
 #pragma unroll
   for (int k = 0; k < kMaskLds / 2; ++k)
-    mword[k] = a.mask[int64_t(u_q) * a.mask_words + min(k, a.mask_words - 1)];
+    mword[k] = load_b64(a.mask + int64_t(u_q) * a.mask_words + min(k, a.mask_words - 1));
 
   // ---- key tiles of the unit: n_pre prefix tiles (the last one may be partial), then the
   // staged tiles.  Stage i of this split holds tiles (s_lo + i) * n_kp + k, k < n_kp, in
@@ -355,10 +383,13 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       wait_vm(n);
   };
 
-  // The first stage's tile loads need only P (a scalar load): issue them now, while the
-  // set-up loads above are in flight, unless P is out of range (checked for every
-  // sequence below, which then raises the error).
-  if (P >= 0 && P <= a.S_max - N && n_st > 0) issue_stage(0);
+  // The first stage's tile loads need only P (a scalar load): issue them now, behind the
+  // set-up loads, unless P is out of range (checked for every sequence below, which then
+  // raises the error).  The rest of the ring is filled once they have landed, so that the
+  // first stage does not share the start-up burst with the next ones.
+  const bool ring_ok = P >= 0 && P <= a.S_max - N && n_st > 0;
+  if (ring_ok) issue_stage(0);
+  const int n_ring_loads = ring_ok ? 2 * kDmaOps * (tile_end(0) - tile_start(0)) : 0;
 
   // ---- RoPE phases (cos, sin) of positions P + d for every depth d < 32: the angle is
   // formed and reduced modulo 2 pi in binary64, then evaluated in fp32.  Thread tid fills
@@ -375,25 +406,26 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     sincosf(r, &sn, &cs);
     s_cs[d][j] = make_float2(cs, sn);
   }
-  // consume them all; the first stage's tile loads, issued above, complete with them, so
-  // that no tile load is in flight at the early exits below
+  // the set-up loads are older than the ring's tile loads, which may stay in flight
+  wait_vm(n_ring_loads);
+  pin(st_word);
+  pin(dep_q_w);
+  pin(dep0_w);
+  pin(P_lane_w);
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    touch(raw[s].x);
-    touch(raw[s].y);
-    touch(raw[s].z);
-    touch(raw[s].w);
+  for (int s = 0; s < 8; ++s) pin(raw[s]);
+#pragma unroll
+  for (int k = 0; k < kMaskLds / 2; ++k) pin(mword[k]);
+  const int dep_q = int(dep_q_w), dep0 = int(dep0_w);
+  const int64_t P_lane = int32_t(P_lane_w);
+  if (st_word != 0) {  // an earlier step of the round failed
+    wait_vm(0);        // no load may still target LDS when the block exits
+    return;
   }
   if (half == 0) {
 #pragma unroll
-    for (int k = 0; k < kMaskLds; ++k)
-      s_mw[wave][k][l32] = k < n_stg ? uint32_t(mword[k >> 1] >> (32 * (k & 1))) : 0u;
+    for (int k = 0; k < kMaskLds; ++k) s_mw[wave][k][l32] = k < n_stg ? mword[k >> 1][k & 1] : 0u;
   }
-  touch(uint32_t(dep_q));
-  touch(uint32_t(dep0));
-  touch(uint32_t(P_lane));
-  wait_vm(0);
-  if (failed) return;
   // every sequence's staged rows [P_b, P_b + N) must lie inside the cache; all blocks
   // evaluate the same condition, so that they all store or none does
   bool unfit = lane < a.B && (P_lane < 0 || P_lane + N > a.S_max);
@@ -402,12 +434,13 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     unfit = unfit || Pb < 0 || Pb + N > a.S_max;
   }
   if (__ballot(unfit)) {
+    wait_vm(0);
     if (blockIdx.x == 0 && tid == 0) raise_status(a.status, MEDUSA_ECAPACITY);
     return;
   }
   if (!live) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) raw[s] = make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < 8; ++s) raw[s] = u32x4{0u, 0u, 0u, 0u};
   }
   bool bad = tid < N && (dep0 < 0 || dep0 >= kTableDepth);
   if (tid < N && tid < kDepthLds) s_dep[tid] = static_cast<unsigned char>(dep0);
@@ -416,10 +449,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     bad = bad || d < 0 || d >= kTableDepth;
     if (i < kDepthLds) s_dep[i] = static_cast<unsigned char>(d);
   }
-
-  // fill the rest of the ring, all but one slot
-  const int first = min(S - 1, n_st);
-  for (int i = 1; i < first; ++i) issue_stage(i);
 
   if (lane == 0) s_bad[wave] = 0;
   if (__ballot(bad) != 0 && lane == 0) s_bad[wave] = 1;
@@ -677,8 +706,10 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
 
   f32x16 s_cur, s_nxt;
   uint32_t b_cur = 0u, b_nxt = 0u;
+  const int first = min(S - 1, n_st);  // stages in flight ahead of the loop
   if (n_st > 0) {
-    wait_stage(0, first - 1);
+    wait_stage(0, 0);
+    for (int i = 1; i < first; ++i) issue_stage(i);  // fill the rest of the ring but one slot
     fix_stage(0);
     __syncthreads();
     prep(0, s_cur, b_cur);
