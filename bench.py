@@ -13,14 +13,15 @@ is reported separately.
 
 Each step uses the next of several independent buffer sets (cache, Q, K/V,
 logits, outputs), together larger than the 256 MB Infinity Cache, so the KV
-stream is served from HBM.  Before its round a set's prefix lengths and status
-word are restored (one 20-byte device copy), so every round runs at the same
-context length.
+stream is served from HBM.  Compaction advances the prefix lengths, so every
+step gets its own prefix-length and status block, filled before timing: every
+round runs at the same context length and the timed loop holds library calls
+only.
 
 Printed on stdout: one JSON line.  ``value`` = verified tree nodes per second
 over the timed steps (B * N per step).  ``roofline`` rates the attention call
-(the dominant kernel): algorithmic bytes per launch / mean launch time from
-dispatch-recorded HIP events, against 8 TB/s.  ``cpu_baseline`` times the CPU
+(the dominant kernels: attention and split merge): algorithmic bytes per call /
+mean call time from HIP events recorded by the two dispatches, against 8 TB/s.  ``cpu_baseline`` times the CPU
 oracle on one round of the same workload.
 """
 import argparse

@@ -97,7 +97,8 @@ typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
  *
  * Errors: MEDUSA_EINVAL (bad field, rank/length out of range, duplicate, rank_hit
  * outside [0,1] or NaN, n_nodes < 1), MEDUSA_ENOT_PREFIX_CLOSED, MEDUSA_ECAPACITY
- * (n_nodes-1 exceeds the number of rank tuples, or n_nodes > 1<<20),
+ * (mode B: n_nodes-1 exceeds the number of rank tuples or n_nodes > 16384; mode
+ * A: 16384 or more explicit paths, i.e. more than 16384 rows),
  * MEDUSA_EBUFSIZE.
  */
 typedef struct {
@@ -149,11 +150,15 @@ medusa_status medusa_tree_compile(const medusa_tree_spec* spec, medusa_tree* out
  * Supported: d_h in {64, 128}; Hq % Hkv == 0; 1 <= N <= 64*mask_words;
  * dt in {MEDUSA_F32, MEDUSA_BF16}.
  * Workspace: device memory of at least medusa_tree_attn_workspace_size(...)
- * bytes.  Its first 4096 bytes are counters that must be zero before the first
- * call; every call leaves them zero again.  Calls sharing a workspace must be
- * ordered (same stream).
+ * bytes, owned by the caller.  For bf16 with d_h = 128 it receives the partial
+ * results of the key-range splits ((m, l) in fp32 and O / l in bf16 per query
+ * row and split), merged into out by a second kernel of the same call; no state
+ * carries from one call to the next.  Calls sharing a workspace must be ordered
+ * (same stream).
  * Device-detected errors (d_status): any P_b < 0 or P_b + N > S_max
- * -> MEDUSA_ECAPACITY, with no stores to the cache or out.
+ * -> MEDUSA_ECAPACITY; for bf16 with d_h = 128, a depth[u] outside [0, 32)
+ * -> MEDUSA_EUNSUPPORTED (the RoPE phase table holds 32 depths); both with no
+ * stores to the cache or out.
  */
 size_t medusa_tree_attn_workspace_size(medusa_dtype dt, int32_t B, int32_t Hq, int32_t Hkv,
                                        int32_t d_h, int32_t N, int32_t S_max);
