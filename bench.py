@@ -145,6 +145,23 @@ def cpu_model():
     return platform.machine()
 
 
+def stream_read_gbs(torch):
+    """STREAM-style read bandwidth of this GPU: a sum over 1 GiB of fp32 (four times the
+    Infinity Cache), timed with events on torch's stream, where the reduction runs."""
+    x = torch.ones(2 ** 28, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        x.sum()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        x.sum()
+    e1.record()
+    e1.synchronize()
+    sec = e0.elapsed_time(e1) / 10 * 1e-3
+    del x
+    return 2 ** 30 / sec / 1e9
+
+
 def cpu_baseline(w, x):
     """The CPU oracle, as it stands, on the same round: every sequence, head and node."""
     import numpy as np
@@ -183,6 +200,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="batched")
+    ap.add_argument("--prefix", type=int, default=0,
+                    help="override the workload's context length P (secondary runs, e.g. llama7b at 4096)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for > 512 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -200,6 +219,9 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
+    if args.prefix:
+        import dataclasses
+        w = dataclasses.replace(w, P=args.prefix)
     spec = workloads.tree_spec(w)
     t0 = time.perf_counter()
     tree = (M.medusa_tree_compile(w.num_heads, w.topk, paths=spec["paths"]) if spec["paths"] is not None
@@ -285,6 +307,7 @@ def main():
         torch.cuda.synchronize()
         copy_info = "torch.neg over 2^26 fp32 (256 MiB read + 256 MiB written) x5"
 
+    stream_gbs = stream_read_gbs(torch)
     esize = 2 if w.dtype == "bf16" else 4
     alg = algorithmic_bytes(w, N, esize)
     mean_s = float(attn_ms.mean()) * 1e-3
@@ -307,13 +330,16 @@ def main():
                      "mean_us": mean_s * 1e6, "median_us": float(np.median(attn_ms)) * 1e3,
                      "p10_us": float(np.percentile(attn_ms, 10)) * 1e3,
                      "p90_us": float(np.percentile(attn_ms, 90)) * 1e3,
-                     "source_hash": src_hash},
+                     "source_hash": src_hash,
+                     "stream_read_gbs": stream_gbs, "frac_of_stream_read": achieved / stream_gbs},
+        "attention_nodes_per_s": w.B * N / mean_s,
         "tree_compile_us": compile_us,
     }
     if copy_info:
         result["copy_calibration"] = copy_info
     log(f"[bench] attention mean {mean_s * 1e6:.2f} us -> {achieved:.0f} GB/s "
-        f"({achieved / HBM_PEAK_GBS:.1%} of HBM peak); step {elapsed / args.steps * 1e6:.1f} us")
+        f"({achieved / HBM_PEAK_GBS:.1%} of HBM peak, {achieved / stream_gbs:.1%} of the "
+        f"{stream_gbs:.0f} GB/s read stream); step {elapsed / args.steps * 1e6:.1f} us")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on one round ...")
         result["cpu_baseline"] = cpu_baseline(w, x)

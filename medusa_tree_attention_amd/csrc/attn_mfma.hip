@@ -120,7 +120,8 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
   p.qrows = kRowsWave * kWaves / p.n_kp;
   p.qblocks = (p.rows + p.qrows - 1) / p.qrows;
   const int32_t wgs = p.units * p.qblocks;
-  int32_t splits = (kTargetWGs + wgs / 2) / wgs;
+  // one workgroup per compute unit at most: a second wave of workgroups would double the time
+  int32_t splits = kTargetWGs / wgs;
   // at least four stages of tiles per split
   const int64_t tiles = (int64_t(S_max) - N + kTile - 1) / kTile + (N + kTile - 1) / kTile;
   const int64_t max_splits = tiles / (4 * p.n_kp);
