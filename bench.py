@@ -202,6 +202,8 @@ def main():
     ap.add_argument("--workload", default="batched")
     ap.add_argument("--prefix", type=int, default=0,
                     help="override the workload's context length P (secondary runs, e.g. llama7b at 4096)")
+    ap.add_argument("--accept", choices=["greedy", "typical"], default="greedy",
+                    help="acceptance rule of the round (typical: temperature 1, epsilon 0.3, alpha 0.09)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for > 512 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -261,22 +263,29 @@ def main():
                 tree["mask_words"], prefix, p(s["q"]), p(s["kn"]), p(s["vn"]), p(s["kc"]),
                 p(s["vc"]), x["S_max"], float(w.rope_base), p(s["out"]), p(s["attn_ws"]),
                 s["attn_ws"].numel(), status]
-        acc = (sptr, w.B, N, w.vocab if x["logits"] is not None else 0, p(s["logits"]), p(s["tids"]),
-               p(s["cand"]), x["candidates"].shape[1], p(shared["tidx"]), p(shared["retrieve"]), nn,
-               width, p(s["best"]), p(s["alen"]), p(s["tokens"]), p(s["frontier"]), p(s["acc_ws"]),
-               s["acc_ws"].numel(), status, None, None)
+        if args.accept == "typical":
+            acc = (sptr, w.B, N, w.vocab, p(s["logits"]), 1.0, 0.3, 0.09, p(s["cand"]),
+                   x["candidates"].shape[1], p(shared["tidx"]), p(shared["retrieve"]), nn, width,
+                   p(s["best"]), p(s["alen"]), p(s["tokens"]), p(s["frontier"]), p(s["acc_ws"]),
+                   s["acc_ws"].numel(), status, None, None)
+        else:
+            acc = (sptr, w.B, N, w.vocab if x["logits"] is not None else 0, p(s["logits"]), p(s["tids"]),
+                   p(s["cand"]), x["candidates"].shape[1], p(shared["tidx"]), p(shared["retrieve"]), nn,
+                   width, p(s["best"]), p(s["alen"]), p(s["tokens"]), p(s["frontier"]), p(s["acc_ws"]),
+                   s["acc_ws"].numel(), status, None, None)
         cmp_ = (sptr, dcode, 1, w.B, w.Hkv, w.d, x["S_max"], N, ctypes.cast(kc_arr, ctypes.c_void_p),
                 ctypes.cast(vc_arr, ctypes.c_void_p), p(shared["retrieve"]), nn, width, p(s["best"]),
                 p(s["alen"]), prefix, status, None, None)
         calls.append((attn, acc, cmp_))
 
+    accept_fn = lib.medusa_accept_typical if args.accept == "typical" else lib.medusa_accept
     ev = HipEvents()
     events = [(ev.create(), ev.create()) for _ in range(total)]
 
     def step(i):
         attn, acc, cmp_ = calls[i]
         rc = lib.medusa_tree_attn(*attn, events[i][0], events[i][1])
-        rc |= lib.medusa_accept(*acc)
+        rc |= accept_fn(*acc)
         rc |= lib.medusa_kv_compact(*cmp_)
         if rc:
             raise RuntimeError(f"library call failed at step {i}")
@@ -323,7 +332,8 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": (f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d_h={w.d}, P={w.P}, "
                                 f"N={N} ({w.tree} tree), V={w.vocab}"),
-                   "global_batch": w.B, "seq_len": w.P, "tree_nodes": N, "buffer_sets": n_sets},
+                   "global_batch": w.B, "seq_len": w.P, "tree_nodes": N, "buffer_sets": n_sets,
+                   "accept": args.accept},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(src_hash),
                      "kernel": "medusa_tree_attn", "algorithmic_bytes": alg,

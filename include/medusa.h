@@ -204,6 +204,37 @@ medusa_status medusa_accept(void* stream, int32_t B, int32_t N, int32_t V, const
                             void* workspace, size_t workspace_bytes, int32_t* d_status,
                             void* ev_start, void* ev_stop);
 
+/* ------------------------------------------------------------------ typical acceptance
+ *
+ * [M7.2] §0x04E "Fast Typical Acceptance Derivation"; defaults from [Chai] section
+ * "接受机制" (posterior_threshold = 0.3 = epsilon, posterior_alpha = 0.09 = alpha).
+ * Per sequence b, with token[u] = candidates[b][tree_indices[u]] as for medusa_accept
+ * and p_r = softmax(logits[b][r] / temperature) for row r:
+ *   H_r    = -sum_x p_r(x) log(p_r(x) + 1e-5)
+ *   tau_r  = min(epsilon, alpha * exp(-H_r))
+ *   edge (r, child) passes iff p_r(token[child]) > tau_r  (strict)
+ *   a_i    = number of leading passing edges of retrieve row i (a sentinel ends it)
+ *   among the i with a_i = max a, the largest sum over its accepted edges of
+ *   log p_r(token[child]) wins; the smallest such i on exact ties.
+ * Outputs and layouts as for medusa_accept (logits are required).  The statistics are
+ * formed in fp32; a pass decision whose margin |p - tau| is below fp32 rounding may differ
+ * from a binary64 evaluation.
+ * Workspace: at least medusa_accept_workspace_size(B, N) bytes of device memory.
+ * Host errors: MEDUSA_EINVAL for temperature <= 0 or a non-finite temperature, epsilon or
+ * alpha, negative epsilon or alpha, or a NULL pointer; MEDUSA_EBUFSIZE for a short
+ * workspace.  Device-detected errors (d_status): a NaN logit, a tree index outside
+ * [0, n_slots), a candidate id outside [0, V), a retrieve entry outside [-1, N) or a path
+ * not starting at row 0 -> MEDUSA_EINVAL, with no output stores.
+ */
+medusa_status medusa_accept_typical(void* stream, int32_t B, int32_t N, int32_t V, const float* logits,
+                                    double temperature, double epsilon, double alpha,
+                                    const int32_t* candidates, int32_t n_slots,
+                                    const int32_t* d_tree_indices, const int32_t* d_retrieve,
+                                    int32_t n_paths, int32_t path_width, int32_t* best_path,
+                                    int32_t* accept_len, int32_t* accepted_tokens,
+                                    int32_t* frontier_row, void* workspace, size_t workspace_bytes,
+                                    int32_t* d_status, void* ev_start, void* ev_stop);
+
 /* ------------------------------------------------------------------ KV compaction
  *
  * [M7.2] §0x06A-§0x06D: with G_b = accept_len[b] + 1, u_j = retrieve[best_path[b]][j],

@@ -5,9 +5,11 @@ The four calls of one verification round, with the names of the C entry points:
     medusa_tree_compile   host tree compiler
     medusa_tree_attn      HIP tree attention (RoPE at P + depth, staged K/V rows)
     medusa_accept         HIP greedy acceptance
+    medusa_accept_typical HIP fast typical acceptance
     medusa_kv_compact     HIP winning-path K/V compaction
 """
 from ._binding import (  # noqa: F401
-    BF16, F32, LIBRARY, MedusaError, STATUS, load, medusa_accept, medusa_accept_workspace_size,
+    BF16, F32, LIBRARY, MedusaError, STATUS, load, medusa_accept, medusa_accept_typical,
+    medusa_accept_workspace_size,
     medusa_kv_compact, medusa_tree_attn, medusa_tree_attn_workspace_size, medusa_tree_compile,
 )

@@ -57,6 +57,8 @@ _SIGNATURES = {
     "medusa_accept_workspace_size": (_SZ, [_I32, _I32]),
     "medusa_accept": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P,
                              _P, _P, _P, _SZ, _P, _P, _P]),
+    "medusa_accept_typical": (_I32, [_P, _I32, _I32, _I32, _P, _D, _D, _D, _P, _I32, _P, _P, _I32,
+                                     _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
     "medusa_kv_compact": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32,
                                  _I32, _P, _P, _P, _P, _P, _P]),
 }
@@ -193,6 +195,22 @@ def medusa_accept(candidates, tree_indices, retrieve, best_path, accept_len, acc
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _ptr(status), ev_start, ev_stop)
     _check("medusa_accept", code)
+
+
+def medusa_accept_typical(candidates, tree_indices, retrieve, best_path, accept_len, accepted_tokens,
+                          frontier_row, status, logits, workspace, temperature=1.0, epsilon=0.3,
+                          alpha=0.09, stream=None, ev_start=None, ev_stop=None):
+    B, n_slots = candidates.shape
+    N = tree_indices.shape[0]
+    V = logits.shape[2]
+    n_paths, width = retrieve.shape
+    code = load().medusa_accept_typical(
+        _stream(stream), B, N, V, _ptr(logits), float(temperature), float(epsilon), float(alpha),
+        _ptr(candidates), n_slots, _ptr(tree_indices), _ptr(retrieve), n_paths, width,
+        _ptr(best_path), _ptr(accept_len), _ptr(accepted_tokens), _ptr(frontier_row),
+        _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _ptr(status), ev_start, ev_stop)
+    _check("medusa_accept_typical", code)
 
 
 # ------------------------------------------------------------------ compaction

@@ -16,8 +16,20 @@
 //                    its piece in the workspace.
 // Kernel 2 (select):  one block per sequence combines the pieces' winners of its rows,
 //                     counts each path's matching prefix and picks the first longest.
+//
+// Fast typical acceptance, [M7.2] §0x04E: p = softmax(logits / T) of the row that
+// scores the next path token, H = -sum p log(p + 1e-5), tau = min(epsilon, alpha
+// exp(-H)); an edge passes when p(c) > tau; a_p counts the leading passes; among the
+// longest, the largest sum of log p(c) over the accepted edges wins, the first on exact
+// ties.  [Chai] "接受机制" gives epsilon = 0.3 and alpha = 0.09.
+// Kernel 1 (row statistics): one 1024-thread block per row keeps the row in registers
+//                    (32 logits per thread) and takes max, sum of exponentials and the
+//                    guarded entropy over them: the row is read from HBM once.
+// Kernel 2 (select):  as above, with the typical edge test and the log-likelihood
+//                     tie-break.
 
 #include <algorithm>
+#include <cmath>
 #include <climits>
 
 #include "common.h"
@@ -35,9 +47,11 @@ struct AcceptArgs {
   int32_t* accepted;          // [B][W]
   int32_t* frontier;          // [B]
   int2* part;                 // workspace [B][N][parts]: (value bits, index) of each piece
+  float4* stats;              // typical: workspace [B][N] (max z, sum 2^(z - max), H, -), base 2
   int32_t* status;
   int32_t B, N, V, n_slots, n_paths, W;
   int32_t parts, chunk4;      // pieces per row; float4 columns per piece (vector path)
+  float inv_temperature, epsilon, alpha;  // typical: inv_temperature = log2(e) / T
 };
 
 __device__ __forceinline__ void keep_better(float& v, int& i, float ov, int oi) {
@@ -121,6 +135,117 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(AcceptArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- typical acceptance
+constexpr int kStatThreads = 1024;
+constexpr int kStatCache = 32;  // logits per thread held in registers: rows up to 32768
+constexpr float kLogGuard = 1e-5f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// block-wide reduction of one value per thread (sum or max), the result in every thread
+template <bool kMax>
+__device__ __forceinline__ float block_reduce(float v, float* scratch) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(v, off, 64);
+    v = kMax ? fmaxf(v, o) : v + o;
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();  // scratch is free
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int w = 1; w < int(blockDim.x >> 6); ++w) r = kMax ? fmaxf(r, scratch[w]) : r + scratch[w];
+  return r;
+}
+
+// Row statistics for fast typical acceptance, in base-2 units so that the hardware exp2 and
+// log2 serve: z = logits log2(e) / T, M = max z, S = sum 2^(z - M), and the entropy
+// H = -ln 2 sum p log2(p + 1e-5) with p = 2^(z - M) / S (the natural-log entropy).  With
+// kCached the row (V <= 32768) stays in registers across the three reductions; longer rows
+// are streamed three times.
+template <bool kCached>
+__global__ __launch_bounds__(kStatThreads) void typical_stats_kernel(AcceptArgs a) {
+  const bool failed = round_failed(a.status);  // gates the stores only
+  __shared__ float scratch[kStatThreads / 64];
+  const int64_t r = blockIdx.x;
+  const float* row = a.logits + r * a.V;
+  const int tid = threadIdx.x;
+  bool nan = false;
+  float M, S, H;
+  if (kCached) {
+    float z[kStatCache];
+    const bool vec = (a.V % 4 == 0) && ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
+    if (vec) {  // thread t holds float4 columns t + 1024 k
+      const float4* row4 = reinterpret_cast<const float4*>(row);
+      const int n4 = a.V / 4;
+#pragma unroll
+      for (int k = 0; k < kStatCache / 4; ++k) {
+        const int c = tid + k * kStatThreads;
+        const float4 x = row4[c < n4 ? c : 0];
+        const bool in = c < n4;
+        z[4 * k] = in ? x.x : -INFINITY;
+        z[4 * k + 1] = in ? x.y : -INFINITY;
+        z[4 * k + 2] = in ? x.z : -INFINITY;
+        z[4 * k + 3] = in ? x.w : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kStatCache; ++k) {
+        const int c = tid + k * kStatThreads;
+        z[k] = c < a.V ? row[c] : -INFINITY;
+      }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kStatCache; ++k) {
+      nan = nan || (z[k] != z[k]);
+      z[k] *= a.inv_temperature;
+      m = fmaxf(m, z[k]);
+    }
+    M = block_reduce<true>(m, scratch);
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kStatCache; ++k) {
+      z[k] = __builtin_amdgcn_exp2f(z[k] - M);  // padding: 2^-inf = 0
+      s += z[k];
+    }
+    S = block_reduce<false>(s, scratch);
+    const float inv_s = 1.0f / S;
+    float h = 0.f;
+#pragma unroll
+    for (int k = 0; k < kStatCache; ++k) {
+      const float pk = z[k] * inv_s;
+      h -= pk * __builtin_amdgcn_logf(pk + kLogGuard);
+    }
+    H = block_reduce<false>(h, scratch) * kLn2;
+  } else {
+    float m = -INFINITY;
+    for (int c = tid; c < a.V; c += kStatThreads) {
+      const float x = row[c];
+      nan = nan || (x != x);
+      m = fmaxf(m, x * a.inv_temperature);
+    }
+    M = block_reduce<true>(m, scratch);
+    float s = 0.f;
+    for (int c = tid; c < a.V; c += kStatThreads) s += __builtin_amdgcn_exp2f(row[c] * a.inv_temperature - M);
+    S = block_reduce<false>(s, scratch);
+    const float inv_s = 1.0f / S;
+    float h = 0.f;
+    for (int c = tid; c < a.V; c += kStatThreads) {
+      const float pk = __builtin_amdgcn_exp2f(row[c] * a.inv_temperature - M) * inv_s;
+      h -= pk * __builtin_amdgcn_logf(pk + kLogGuard);
+    }
+    H = block_reduce<false>(h, scratch) * kLn2;
+  }
+  const bool any_nan = __syncthreads_or(nan);
+  if (tid == 0 && !failed) {
+    if (any_nan)
+      raise_status(a.status, MEDUSA_EINVAL);
+    else
+      a.stats[r] = make_float4(M, S, H, 0.f);
+  }
+}
+
 // target token of row u of sequence b: the winner over the row's pieces (the lowest index
 // among equal values), or the given id
 __device__ __forceinline__ int32_t row_target(const AcceptArgs& a, int b, int u) {
@@ -138,8 +263,10 @@ __device__ __forceinline__ int32_t row_target(const AcceptArgs& a, int b, int u)
 // that the path walks below make no dependent global loads; trees too large for that read
 // them from memory.  The tree buffers must name valid slots and rows, and every retrieve
 // row must start at the root and be padded only at its end; all blocks see the same
-// buffers and reach the same verdict.
-template <bool kStaged>
+// buffers and reach the same verdict.  kTypical selects the typical edge test (candidate
+// ids must then be tokens of the vocabulary: they index the logits) and ranks paths of
+// equal length by their summed log p.
+template <bool kStaged, bool kTypical>
 __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
   const bool failed = round_failed(a.status);  // gates the stores only
   const int b = blockIdx.x;
@@ -153,7 +280,7 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
     int32_t* s_cand = s_tix + a.N;
     int32_t* s_ret = s_cand + a.n_slots;
     for (int u = threadIdx.x; u < a.N; u += blockDim.x) {
-      s_tgt[u] = row_target(a, b, u);
+      if (!kTypical) s_tgt[u] = row_target(a, b, u);
       s_tix[u] = tix[u];
     }
     for (int i = threadIdx.x; i < a.n_slots; i += blockDim.x) s_cand[i] = cand[i];
@@ -167,6 +294,9 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
 
   bool ok = true;
   for (int u = threadIdx.x; u < a.N; u += blockDim.x) ok = ok && tix[u] >= 0 && tix[u] < a.n_slots;
+  if (kTypical)  // every sequence's candidates, so that all blocks reach the same verdict
+    for (int i = threadIdx.x; i < a.B * a.n_slots; i += blockDim.x)
+      ok = ok && a.candidates[i] >= 0 && a.candidates[i] < a.V;
   for (int i = threadIdx.x; i < a.n_paths; i += blockDim.x) {
     const int32_t* r = ret + int64_t(i) * a.W;
     ok = ok && r[0] == 0;
@@ -182,40 +312,63 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
     return;
   }
 
+  // (length, summed log p, -index), compared lexicographically; greedy paths carry 0
+  auto better = [](int l, float ll, int i, int bl, float bll, int bi) {
+    return l > bl || (l == bl && (ll > bll || (ll == bll && i < bi)));
+  };
   int best_len = -1, best_i = INT_MAX;
+  float best_ll = -INFINITY;
   for (int i = threadIdx.x; i < a.n_paths; i += blockDim.x) {
     const int32_t* r = ret + int64_t(i) * a.W;
     int len = 0;
+    float ll = 0.f;
     for (int j = 0; j + 1 < a.W; ++j) {
       const int nxt = r[j + 1];
-      if (nxt < 0 || cand[tix[nxt]] != tgt(r[j])) break;
+      if (nxt < 0) break;
+      const int c = cand[tix[nxt]];
+      if (kTypical) {
+        const int64_t row = int64_t(b) * a.N + r[j];
+        const float4 st = a.stats[row];
+        const float pc = __builtin_amdgcn_exp2f(a.logits[row * a.V + c] * a.inv_temperature - st.x) / st.y;
+        const float tau = fminf(a.epsilon, a.alpha * expf(-st.z));
+        if (!(pc > tau)) break;
+        ll += __builtin_amdgcn_logf(pc) * kLn2;
+      } else if (c != tgt(r[j])) {
+        break;
+      }
       ++len;
     }
-    if (len > best_len || (len == best_len && i < best_i)) {
+    if (better(len, ll, i, best_len, best_ll, best_i)) {
       best_len = len;
+      best_ll = ll;
       best_i = i;
     }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const int ol = __shfl_xor(best_len, off, 64);
+    const float oll = __shfl_xor(best_ll, off, 64);
     const int oi = __shfl_xor(best_i, off, 64);
-    if (ol > best_len || (ol == best_len && oi < best_i)) {
+    if (better(ol, oll, oi, best_len, best_ll, best_i)) {
       best_len = ol;
+      best_ll = oll;
       best_i = oi;
     }
   }
   __shared__ int sl[4], si[4];
+  __shared__ float sll[4];
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   if (lane == 0) {
     sl[wave] = best_len;
+    sll[wave] = best_ll;
     si[wave] = best_i;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < int(blockDim.x / 64); ++w) {
-      if (sl[w] > sl[0] || (sl[w] == sl[0] && si[w] < si[0])) {
+      if (better(sl[w], sll[w], si[w], sl[0], sll[0], si[0])) {
         sl[0] = sl[w];
+        sll[0] = sll[w];
         si[0] = si[w];
       }
     }
@@ -299,7 +452,57 @@ extern "C" medusa_status medusa_accept(void* stream, int32_t B, int32_t N, int32
     if (st != MEDUSA_OK) return st;
     ev_start = nullptr;
   }
-  const void* sel = staged ? reinterpret_cast<const void*>(&select_kernel<true>)
-                           : reinterpret_cast<const void*>(&select_kernel<false>);
+  const void* sel = staged ? reinterpret_cast<const void*>(&select_kernel<true, false>)
+                           : reinterpret_cast<const void*>(&select_kernel<false, false>);
   return launch(sel, dim3(B), dim3(256), staged ? lds : 0, s, a, ev_start, ev_stop);
+}
+
+extern "C" medusa_status medusa_accept_typical(void* stream, int32_t B, int32_t N, int32_t V,
+                                               const float* logits, double temperature, double epsilon,
+                                               double alpha, const int32_t* candidates, int32_t n_slots,
+                                               const int32_t* d_tree_indices, const int32_t* d_retrieve,
+                                               int32_t n_paths, int32_t path_width, int32_t* best_path,
+                                               int32_t* accept_len, int32_t* accepted_tokens,
+                                               int32_t* frontier_row, void* workspace, size_t workspace_bytes,
+                                               int32_t* d_status, void* ev_start, void* ev_stop) {
+  if (B < 1 || N < 1 || V < 1 || n_slots < 1 || n_paths < 1 || path_width < 1) return MEDUSA_EINVAL;
+  if (!(temperature > 0.0) || !(epsilon >= 0.0) || !(alpha >= 0.0) || !std::isfinite(temperature) ||
+      !std::isfinite(epsilon) || !std::isfinite(alpha))
+    return MEDUSA_EINVAL;
+  if (!logits || !candidates || !d_tree_indices || !d_retrieve || !best_path || !accept_len ||
+      !accepted_tokens || !frontier_row || !d_status)
+    return MEDUSA_EINVAL;
+  if (workspace == nullptr || workspace_bytes < medusa_accept_workspace_size(B, N)) return MEDUSA_EBUFSIZE;
+
+  AcceptArgs a{};
+  a.logits = logits;
+  a.candidates = candidates;
+  a.tree_indices = d_tree_indices;
+  a.retrieve = d_retrieve;
+  a.best_path = best_path;
+  a.accept_len = accept_len;
+  a.accepted = accepted_tokens;
+  a.frontier = frontier_row;
+  a.stats = static_cast<float4*>(workspace);
+  a.status = d_status;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.n_slots = n_slots;
+  a.n_paths = n_paths;
+  a.W = path_width;
+  a.parts = 1;
+  a.inv_temperature = float(1.4426950408889634 / temperature);
+  a.epsilon = float(epsilon);
+  a.alpha = float(alpha);
+  const size_t lds = (2 * size_t(N) + size_t(n_slots) + size_t(n_paths) * path_width) * sizeof(int32_t);
+  const bool staged = lds <= kSelectLds;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* stats = V <= kStatThreads * kStatCache ? reinterpret_cast<const void*>(&typical_stats_kernel<true>)
+                                                     : reinterpret_cast<const void*>(&typical_stats_kernel<false>);
+  medusa_status st = launch(stats, dim3(unsigned(int64_t(B) * N)), dim3(kStatThreads), 0, s, a, ev_start, nullptr);
+  if (st != MEDUSA_OK) return st;
+  const void* sel = staged ? reinterpret_cast<const void*>(&select_kernel<true, true>)
+                           : reinterpret_cast<const void*>(&select_kernel<false, true>);
+  return launch(sel, dim3(B), dim3(256), staged ? lds : 0, s, a, nullptr, ev_stop);
 }
