@@ -14,6 +14,7 @@ computed in IEEE binary64 unless the operation is integer-only:
 * ``accept``     -- greedy longest-prefix acceptance (two independent ways)
 * ``typical``    -- fast typical acceptance
 * ``compact``    -- winning-path K/V compaction with a snapshot
+* ``heads``      -- the Medusa head step and the ranked candidate pool
 
 Pages cited (by title and section):
 
@@ -23,4 +24,4 @@ Pages cited (by title and section):
 [Math]  "Medusa — Multi-Head Speculative Decoding Math"
 """
 
-from . import tree, attention, accept, compact, typical  # noqa: F401
+from . import tree, attention, accept, compact, typical, heads  # noqa: F401

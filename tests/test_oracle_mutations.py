@@ -11,10 +11,12 @@ import pytest
 import test_oracle_accept as PA
 import test_oracle_attention as PT
 import test_oracle_compact as PC
+import test_oracle_heads as PH
 import test_oracle_tree as PR
 from oracle import accept as AC
 from oracle import attention as A
 from oracle import compact as C
+from oracle import heads as HD
 from oracle import tree as T
 from oracle import typical as TY
 
@@ -214,3 +216,51 @@ def test_in_place_reverse_copy_is_caught(monkeypatch):
         return np.array([int(p) + int(a) + 1 for p, a in zip(prefix_len, accept_len)], np.int32)
     monkeypatch.setattr(C, "kv_compact", no_snapshot)
     must_fail(PC.test_a31_commit_trace)
+
+
+# ---------------------------------------------------------------- head step
+
+def test_sigmoid_instead_of_silu_is_caught(monkeypatch):
+    monkeypatch.setattr(HD, "silu", lambda x: 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64))))
+    must_fail(PH.test_silu_limits_not_sigmoid)
+    must_fail(PH.test_zero_residual_projection_is_the_unembedding)
+
+
+def test_missing_residual_is_caught(monkeypatch):
+    def no_residual(h, W1, W2):
+        h = np.asarray(h, np.float64)
+        return np.asarray(W2, np.float64) @ HD.silu(np.asarray(W1, np.float64) @ h)
+    monkeypatch.setattr(HD, "head_logits", no_residual)
+    must_fail(PH.test_zero_residual_projection_is_the_unembedding)
+
+
+def test_transposed_residual_projection_is_caught(monkeypatch):
+    def transposed(h, W1, W2):
+        h = np.asarray(h, np.float64)
+        return np.asarray(W2, np.float64) @ (HD.silu(np.asarray(W1, np.float64).T @ h) + h)
+    monkeypatch.setattr(HD, "head_logits", transposed)
+    must_fail(PH.test_residual_projection_orientation)
+
+
+def test_tie_to_higher_index_is_caught(monkeypatch):
+    def higher_first(row, k):
+        row = np.asarray(row, np.float64)
+        order = sorted(range(row.shape[0]), key=lambda i: (-row[i], -i))
+        return order[:k]
+    monkeypatch.setattr(HD, "top_ranked", higher_first)
+    must_fail(PH.test_ranking_matches_its_definition_by_brute_force, 0)
+
+
+def test_slot_of_wrong_head_is_caught(monkeypatch):
+    real = HD.head_candidates
+
+    def shifted(h, W1, W2, root, topk):
+        res = real(h, W1, W2, root, topk)
+        c = res["candidates"]
+        K = len(W1)
+        heads = c[:, 1:].reshape(c.shape[0], K, topk)[:, ::-1].reshape(c.shape[0], -1)   # heads reversed
+        res["candidates"] = np.concatenate([c[:, :1], heads], axis=1)
+        return res
+    monkeypatch.setattr(HD, "head_candidates", shifted)
+    must_fail(PH.test_candidate_slots_feed_the_tree_gather)
+
