@@ -4,10 +4,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
 
 A step is one whole round over one batch of synthetic inputs already resident
-in HBM: ``medusa_tree_attn`` (RoPE at P + depth, staged K/V rows, tree
+in HBM.  By default (``--round verify``) that is ``medusa_tree_attn`` (RoPE at P + depth, staged K/V rows, tree
 attention), ``medusa_accept`` (greedy acceptance over fp32 target logits) and
 ``medusa_kv_compact`` (winning-path K/V gather), on one stream with no host
-synchronisation.  The tree itself is compiled once on the host before the
+synchronisation.  ``--round full`` runs the batched full round: the Medusa head
+step ``medusa_head_candidates`` (W2 (SiLU(W1 h) + h) for four heads, top-10 of
+each, candidate rows written on the device) comes first in every step and
+fills the candidates that the acceptance reads.  The tree itself is compiled once on the host before the
 timed region (the buffers are static for a tree shape) and its compile time
 is reported separately.
 
@@ -22,7 +25,9 @@ Printed on stdout: one JSON line.  ``value`` = verified tree nodes per second
 over the timed steps (B * N per step).  ``roofline`` rates the attention call
 (the dominant kernels: attention and split merge): algorithmic bytes per call /
 mean call time from HIP events recorded by the two dispatches, against 8 TB/s.  ``cpu_baseline`` times the CPU
-oracle on one round of the same workload.
+oracle on one round of the same workload.  With ``--round full`` the head call
+is the dominant one and ``roofline`` rates it (weights, h and candidate rows per
+call); the attention figures move to ``attention_roofline``.
 """
 import argparse
 import ctypes
@@ -40,19 +45,29 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 ATTN_SOURCES = ["attn.hip", "attn_mfma.hip", "attn_common.h", "common.h"]
+HEAD_SOURCES = ["heads.hip", "common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_batched.md")
+HEAD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "head_step_traffic_batched.md")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def attn_source_hash():
+def source_hash(files):
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "medusa_tree_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def attn_source_hash():
+    return source_hash(ATTN_SOURCES)
+
+
+def head_source_hash():
+    return source_hash(HEAD_SOURCES)
 
 
 def algorithmic_bytes(w, N, esize):
@@ -63,12 +78,18 @@ def algorithmic_bytes(w, N, esize):
     return prefix_kv + q + new_kv + staged + o
 
 
-def measured_traffic(src_hash):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def head_algorithmic_bytes(B, K, hidden, V, topk):
+    """Bytes the head step must move: both weight sets of every head once, h, the root
+    tokens and the candidate rows (the u vectors and the logits are intermediates)."""
+    return 2 * K * (hidden * hidden + V * hidden) + 2 * B * hidden + 4 * B + 4 * B * (1 + K * topk)
+
+
+def measured_traffic(src_hash, path=TRAFFIC_FILE):
+    """HBM bytes per call from a committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources."""
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE, encoding="utf-8").read()
+    text = open(path, encoding="utf-8").read()
     m_hash = re.search(r"kernel source hash:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"scaled HBM bytes per launch:\s*([0-9]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
@@ -162,8 +183,9 @@ def stream_read_gbs(torch):
     return 2 ** 30 / sec / 1e9
 
 
-def cpu_baseline(w, x):
-    """The CPU oracle, as it stands, on the same round: every sequence, head and node."""
+def cpu_baseline(w, x, xh=None):
+    """The CPU oracle, as it stands, on the same round: every sequence, head and node (and,
+    given the head inputs ``xh``, the head step that fills the candidates first)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -171,16 +193,20 @@ def cpu_baseline(w, x):
     from oracle import accept as AC
     from oracle import attention as A
     from oracle import compact as C
+    from oracle import heads as HD
     from oracle import tree as T
 
     spec = workloads.tree_spec(w)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
+        cand = x["candidates"]
+        if xh is not None:
+            cand = HD.head_candidates(xh["h"], xh["W1"], xh["W2"], xh["root_tokens"], w.topk)["candidates"]
         ora = (T.compile_tree(spec["paths"], w.num_heads, w.topk) if spec["paths"] is not None
                else T.compile_greedy(spec["rank_hit"], spec["n_nodes"]))
         _, sk, sv = A.tree_attention(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
                                      x["prefix_len"], ora["depth"], ora["parent"], w.rope_base)
-        res = AC.accept_batch(ora, x["candidates"], logits=x["logits"], target_ids=x["target_ids"])
+        res = AC.accept_batch(ora, cand, logits=x["logits"], target_ids=x["target_ids"])
         cache = [np.array(x["k_cache"], np.float64), np.array(x["v_cache"], np.float64)]
         for b in range(w.B):
             P = int(x["prefix_len"][b])
@@ -190,7 +216,8 @@ def cpu_baseline(w, x):
         dt = time.perf_counter() - t0
     return {"value": w.B * x["N"] / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
             "sample": (f"one full round of the workload ({w.B} sequences x {x['N']} nodes x {w.Hq} heads "
-                       f"at P={w.P}): tree compile, per-path binary64 attention, greedy accept, "
+                       f"at P={w.P}): " + ("binary64 head step (4 heads, top-k), " if xh is not None else "")
+                       + f"tree compile, per-path binary64 attention, greedy accept, "
                        f"compaction; {dt:.1f} s on 1 thread of {cpu_model()}")}
 
 
@@ -204,6 +231,8 @@ def main():
                     help="override the workload's context length P (secondary runs, e.g. llama7b at 4096)")
     ap.add_argument("--accept", choices=["greedy", "typical"], default="greedy",
                     help="acceptance rule of the round (typical: temperature 1, epsilon 0.3, alpha 0.09)")
+    ap.add_argument("--round", choices=["verify", "full"], default="verify",
+                    help="full: the Medusa head step fills the candidates first in every step")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for > 512 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -237,6 +266,19 @@ def main():
     n_sets = args.sets or max(2, -(-512 * 2 ** 20 // per_set))
     shared, pristine, sets = build_sets(w, x, tree, n_sets, torch, M)
     log(f"[bench] workload={w.name} N={N} sets={n_sets} x {per_set / 2**20:.1f} MiB")
+    xh = heads = None
+    hidden = w.Hq * w.d
+    if args.round == "full":
+        # one copy of the head weights (1.18 GB at hidden 4096, V 32000: four times the
+        # Infinity Cache, so every step reads them from HBM)
+        xh = workloads.draw_heads(w.seed + 300, w.B, w.num_heads, hidden, w.vocab)
+        hb = M.medusa_head_workspace_size(w.B, w.num_heads, hidden, w.vocab)
+        heads = {"h": torch.from_numpy(xh["h"]).to("cuda", torch.bfloat16),
+                 "W1": torch.from_numpy(xh["W1"]).to("cuda", torch.bfloat16),
+                 "W2": torch.from_numpy(xh["W2"]).to("cuda", torch.bfloat16),
+                 "root": torch.from_numpy(xh["root_tokens"]).to("cuda"),
+                 "ws": torch.zeros(hb, dtype=torch.uint8, device="cuda")}
+        log(f"[bench] head step: K={w.num_heads} hidden={hidden} V={w.vocab} topk={w.topk}")
 
     lib = M.load()
     stream = torch.cuda.current_stream()
@@ -276,15 +318,24 @@ def main():
         cmp_ = (sptr, dcode, 1, w.B, w.Hkv, w.d, x["S_max"], N, ctypes.cast(kc_arr, ctypes.c_void_p),
                 ctypes.cast(vc_arr, ctypes.c_void_p), p(shared["retrieve"]), nn, width, p(s["best"]),
                 p(s["alen"]), prefix, status, None, None)
-        calls.append((attn, acc, cmp_))
+        head = None
+        if heads is not None:
+            head = (sptr, w.B, w.num_heads, hidden, w.vocab, w.topk, p(heads["h"]), p(heads["W1"]),
+                    p(heads["W2"]), p(heads["root"]), p(s["cand"]), None, p(heads["ws"]),
+                    heads["ws"].numel(), status)
+        calls.append((attn, acc, cmp_, head))
 
     accept_fn = lib.medusa_accept_typical if args.accept == "typical" else lib.medusa_accept
     ev = HipEvents()
     events = [(ev.create(), ev.create()) for _ in range(total)]
+    head_events = [(ev.create(), ev.create()) for _ in range(total)] if heads is not None else []
 
     def step(i):
-        attn, acc, cmp_ = calls[i]
-        rc = lib.medusa_tree_attn(*attn, events[i][0], events[i][1])
+        attn, acc, cmp_, head = calls[i]
+        rc = 0
+        if head is not None:
+            rc |= lib.medusa_head_candidates(*head, head_events[i][0], head_events[i][1])
+        rc |= lib.medusa_tree_attn(*attn, events[i][0], events[i][1])
         rc |= accept_fn(*acc)
         rc |= lib.medusa_kv_compact(*cmp_)
         if rc:
@@ -303,7 +354,8 @@ def main():
     if statuses.any():
         raise RuntimeError(f"device status words {sorted(set(statuses.tolist()))}: the round failed")
     attn_ms = np.array([ev.elapsed_ms(a, b) for a, b in events[args.warmup:]])
-    for a, b in events:
+    head_ms = np.array([ev.elapsed_ms(a, b) for a, b in head_events[args.warmup:]])
+    for a, b in events + head_events:
         ev.destroy(a)
         ev.destroy(b)
 
@@ -333,7 +385,7 @@ def main():
         "config": {"workload": (f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d_h={w.d}, P={w.P}, "
                                 f"N={N} ({w.tree} tree), V={w.vocab}"),
                    "global_batch": w.B, "seq_len": w.P, "tree_nodes": N, "buffer_sets": n_sets,
-                   "accept": args.accept},
+                   "accept": args.accept, "round": args.round},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(src_hash),
                      "kernel": "medusa_tree_attn", "algorithmic_bytes": alg,
@@ -345,6 +397,24 @@ def main():
         "attention_nodes_per_s": w.B * N / mean_s,
         "tree_compile_us": compile_us,
     }
+    if heads is not None:
+        h_alg = head_algorithmic_bytes(w.B, w.num_heads, hidden, w.vocab, w.topk)
+        h_mean = float(head_ms.mean()) * 1e-3
+        h_ach = h_alg / h_mean / 1e9
+        h_hash = head_source_hash()
+        result["attention_roofline"] = result.pop("roofline")
+        result["roofline"] = {
+            "bound": "hbm", "achieved": h_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": h_ach / HBM_PEAK_GBS, "traffic": measured_traffic(h_hash, HEAD_TRAFFIC_FILE),
+            "kernel": "medusa_head_candidates", "algorithmic_bytes": h_alg,
+            "mean_us": h_mean * 1e6, "median_us": float(np.median(head_ms)) * 1e3,
+            "p10_us": float(np.percentile(head_ms, 10)) * 1e3,
+            "p90_us": float(np.percentile(head_ms, 90)) * 1e3,
+            "source_hash": h_hash, "stream_read_gbs": stream_gbs,
+            "frac_of_stream_read": h_ach / stream_gbs}
+        result["config"]["workload"] += f"; head step K={w.num_heads}, hidden={hidden}, topk={w.topk}"
+        log(f"[bench] head step mean {h_mean * 1e6:.2f} us -> {h_ach:.0f} GB/s "
+            f"({h_ach / HBM_PEAK_GBS:.1%} of HBM peak, {h_ach / stream_gbs:.1%} of the read stream)")
     if copy_info:
         result["copy_calibration"] = copy_info
     log(f"[bench] attention mean {mean_s * 1e6:.2f} us -> {achieved:.0f} GB/s "
@@ -352,7 +422,7 @@ def main():
         f"{stream_gbs:.0f} GB/s read stream); step {elapsed / args.steps * 1e6:.1f} us")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on one round ...")
-        result["cpu_baseline"] = cpu_baseline(w, x)
+        result["cpu_baseline"] = cpu_baseline(w, x, xh)
     print(json.dumps(result), flush=True)
 
 

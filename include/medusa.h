@@ -235,6 +235,40 @@ medusa_status medusa_accept_typical(void* stream, int32_t B, int32_t N, int32_t 
                                     int32_t* frontier_row, void* workspace, size_t workspace_bytes,
                                     int32_t* d_status, void* ev_start, void* ev_stop);
 
+/* ------------------------------------------------------------------ head step and candidates
+ *
+ * [Chai] section "Medusa 的核心思路与系统位置" and [Math] section "The Medusa head: math and
+ * shapes": head k maps the last hidden state h of sequence b to the logits
+ *   l_k[b] = W2_k (SiLU(W1_k h_b) + h_b)       (no bias; [M7.2] §0x02A adds one in general)
+ * "Medusa Part II ...", Part 4: each head contributes its topk ranked ids; [M7.2] §0x01B:
+ *   candidates[b][0]                   = root_tokens[b]   (the LM head's token, [Chai]
+ *                                                          "一次完整解码迭代")
+ *   candidates[b][1 + k*topk + r]      = id of the r-th largest entry of l_k[b]
+ * the lower id first among equal logits.  This is the candidates[] input of medusa_accept.
+ * Layouts (bf16 = IEEE binary32 truncated to its high 16 bits with round-to-nearest-even):
+ *   h          bf16 [B][d]      device (16-byte aligned)
+ *   W1         bf16 [K][d][d]   device, row o of head k is W1_k[o][:] (16-byte aligned)
+ *   W2         bf16 [K][V][d]   device, row v of head k is W2_k[v][:] (16-byte aligned)
+ *   d_root_tokens int32 [B]; candidates int32 [B][1 + K*topk]; device
+ *   head_logits   optional fp32 [K][B][V] device output (NULL: kept in the workspace)
+ * Arithmetic in fp32 (inputs widened, products accumulated in fp32).  Weights are read once
+ * per group of four sequences.
+ * Workspace: at least medusa_head_workspace_size(B, K, d, V) bytes of device memory; it
+ * receives u = SiLU(W1 h) + h and, without head_logits, the logits.
+ * Host errors: MEDUSA_EINVAL (non-positive size, NULL pointer, h, W1 or W2 not 16-byte
+ * aligned), MEDUSA_EUNSUPPORTED (d not a multiple of 8 or above 8192, topk above 64 or above
+ * V, one head's W2 or the fp32 inputs of one head 4 GiB or larger), MEDUSA_EBUFSIZE.
+ * Device-detected error (d_status): a NaN logit -> MEDUSA_EINVAL, and no candidate is written
+ * by a call whose status word is already nonzero when its last kernel starts.
+ */
+size_t medusa_head_workspace_size(int32_t B, int32_t K, int32_t d, int32_t V);
+
+medusa_status medusa_head_candidates(void* stream, int32_t B, int32_t K, int32_t d, int32_t V,
+                                     int32_t topk, const void* h, const void* W1, const void* W2,
+                                     const int32_t* d_root_tokens, int32_t* candidates,
+                                     float* head_logits, void* workspace, size_t workspace_bytes,
+                                     int32_t* d_status, void* ev_start, void* ev_stop);
+
 /* ------------------------------------------------------------------ KV compaction
  *
  * [M7.2] §0x06A-§0x06D: with G_b = accept_len[b] + 1, u_j = retrieve[best_path[b]][j],

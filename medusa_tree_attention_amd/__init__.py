@@ -7,9 +7,10 @@ The four calls of one verification round, with the names of the C entry points:
     medusa_accept         HIP greedy acceptance
     medusa_accept_typical HIP fast typical acceptance
     medusa_kv_compact     HIP winning-path K/V compaction
+    medusa_head_candidates HIP Medusa head step and ranked candidate pool
 """
 from ._binding import (  # noqa: F401
     BF16, F32, LIBRARY, MedusaError, STATUS, load, medusa_accept, medusa_accept_typical,
-    medusa_accept_workspace_size,
+    medusa_accept_workspace_size, medusa_head_candidates, medusa_head_workspace_size,
     medusa_kv_compact, medusa_tree_attn, medusa_tree_attn_workspace_size, medusa_tree_compile,
 )

@@ -59,6 +59,9 @@ _SIGNATURES = {
                              _P, _P, _P, _SZ, _P, _P, _P]),
     "medusa_accept_typical": (_I32, [_P, _I32, _I32, _I32, _P, _D, _D, _D, _P, _I32, _P, _P, _I32,
                                      _I32, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
+    "medusa_head_workspace_size": (_SZ, [_I32] * 4),
+    "medusa_head_candidates": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                      _SZ, _P, _P, _P]),
     "medusa_kv_compact": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32,
                                  _I32, _P, _P, _P, _P, _P, _P]),
 }
@@ -211,6 +214,24 @@ def medusa_accept_typical(candidates, tree_indices, retrieve, best_path, accept_
         _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _ptr(status), ev_start, ev_stop)
     _check("medusa_accept_typical", code)
+
+
+# ------------------------------------------------------------------ head step
+
+def medusa_head_workspace_size(B, K, d, V):
+    return int(load().medusa_head_workspace_size(B, K, d, V))
+
+
+def medusa_head_candidates(h, W1, W2, root_tokens, candidates, status, workspace, topk,
+                           head_logits=None, stream=None, ev_start=None, ev_stop=None):
+    B, d = h.shape
+    K, V = W2.shape[0], W2.shape[1]
+    code = load().medusa_head_candidates(
+        _stream(stream), B, K, d, V, topk, _ptr(h), _ptr(W1), _ptr(W2), _ptr(root_tokens),
+        _ptr(candidates), _ptr(head_logits), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _ptr(status), ev_start, ev_stop)
+    _check("medusa_head_candidates", code)
 
 
 # ------------------------------------------------------------------ compaction

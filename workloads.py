@@ -25,7 +25,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "rank_hit_table", "cartesian_paths",
-    "round_to_dtype", "draw_round", "plant_acceptance", "tree_spec",
+    "round_to_dtype", "draw_round", "plant_acceptance", "tree_spec", "draw_heads",
 ]
 
 
@@ -118,10 +118,14 @@ def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
         return x
     if dtype != "bf16":
         raise ValueError(dtype)
-    bits = x.view(np.uint32).astype(np.uint64)
-    # round-to-nearest-even on the upper 16 bits (inputs are finite draws)
-    rounded = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
-    return (rounded.astype(np.uint32) << 16).view(np.float32)
+    bits = x.view(np.uint32)
+    # round-to-nearest-even on the upper 16 bits; for finite inputs the sum stays below
+    # 2^32 (the largest finite pattern 0xFF7FFFFF + 0x8000 = 0xFF807FFF)
+    out = (bits >> 16) & np.uint32(1)
+    out += np.uint32(0x7FFF)
+    out += bits
+    out &= np.uint32(0xFFFF0000)
+    return out.view(np.float32)
 
 
 def _node_count(w: Workload) -> int:
@@ -218,3 +222,34 @@ def plant_acceptance(rng: np.random.Generator, inputs: dict, tokens: np.ndarray,
             tid[rows[j]] = tokens[rows[j + 1]]
         choices = [t for t in range(int(inputs["vocab"])) if t not in child_tokens]
         tid[stop] = choices[int(rng.integers(0, len(choices)))]
+
+
+def draw_heads(seed: int, B: int, K: int, hidden: int, vocab: int,
+               w1_std: float = 0.002, w2_std: float = 0.02) -> dict:
+    """Inputs of the Medusa head step, bf16-exact values held in float32.
+
+    h            [B, hidden]            ~N(0, 1)            (the last hidden states)
+    W1           [K, hidden, hidden]    ~N(0, w1_std^2)     (one matrix per head)
+    W2           [K, vocab, hidden]     ~N(0, w2_std^2)
+    root_tokens  [B] int32 uniform in [0, vocab)
+    The default standard deviations are those of the batched full round (0.002 and 0.02).
+    Draw order: h, then per head W1_k and W2_k (in blocks of 4096 rows), then the root
+    tokens.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    h = round_to_dtype(rng.standard_normal((B, hidden), dtype=np.float32), "bf16")
+    W1 = np.empty((K, hidden, hidden), np.float32)
+    W2 = np.empty((K, vocab, hidden), np.float32)
+
+    def fill(dst, std):
+        for r0 in range(0, dst.shape[0], 4096):
+            blk = dst[r0:r0 + 4096]
+            rng.standard_normal(dtype=np.float32, out=blk)
+            blk *= np.float32(std)
+            blk[...] = round_to_dtype(blk, "bf16")
+
+    for k in range(K):
+        fill(W1[k], w1_std)
+        fill(W2[k], w2_std)
+    root = rng.integers(0, vocab, size=B).astype(np.int32)
+    return {"h": h, "W1": W1, "W2": W2, "root_tokens": root}
