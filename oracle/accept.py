@@ -13,7 +13,10 @@ Follows:
 * [PartII] Part 7 "Exact Greedy Verification and Rejection": the same
   cumulative-product rule; "Padded paths are not real completions".
 * [M7.2] §0x06C "The Terminal Row Carries The Next Frontier": the frontier is
-  row retrieve[p*, a].
+  row retrieve[p*, a]; the next round's target and head distributions are those
+  produced at that row (conditioned on exactly the committed history), so the
+  next root is the target's greedy token there and the next head step reads the
+  hidden state of that row.
 
 Readings: argmax ties go to the lowest vocabulary index; a NaN logit makes
 the round invalid; a sentinel (-1) ends a path and never matches.
@@ -124,4 +127,19 @@ def accept_batch(tree: dict, candidates, logits=None, target_ids=None) -> dict:
         out["accepted_tokens"][b, : len(res["accepted_tokens"])] = res["accepted_tokens"]
         out["frontier_row"][b] = res["frontier_row"]
         out["target"][b] = target
+    return out
+
+
+def frontier_carry(result: dict, hidden=None) -> dict:
+    """The state the next round starts from, for every sequence of an accept_batch result.
+
+    next_root[b] = target[b][frontier_row[b]] (the target's greedy token after the last
+    accepted input); with hidden [B][N][H], h_next[b] = hidden[b][frontier_row[b]].
+    """
+    B = len(result["frontier_row"])
+    out = {"next_root": np.array([int(result["target"][b][int(result["frontier_row"][b])])
+                                  for b in range(B)], np.int32)}
+    if hidden is not None:
+        hidden = np.asarray(hidden)
+        out["h_next"] = np.stack([hidden[b, int(result["frontier_row"][b])] for b in range(B)])
     return out

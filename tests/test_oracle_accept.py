@@ -129,6 +129,56 @@ def test_planted_acceptance_recovers_planted_depth(name):
         assert rows == [int(r) for r in t["retrieve"][path, : depth + 1]]
 
 
+# ---------------------------------------------------------------- frontier carry
+
+@pytest.mark.parametrize("seed,paths", [
+    (0, [(0,), (1,), (0, 0), (0, 1), (1, 0), (1, 1)]),
+    (2, [(0,), (1,), (0, 0), (0, 0, 0), (0, 0, 1)]),
+])
+def test_frontier_carry_is_where_the_tree_walk_stops(seed, paths):
+    """[M7.2] §0x06C: the next round starts from the row after the last accepted input.
+    The tree walk (an independent algorithm) stops at a row whose target token no child
+    carries: that row must be the frontier, and the token it stops on the next root."""
+    rng = np.random.default_rng(seed)
+    K, TOPK, V = 3, 2, 3
+    t = T.compile_tree(paths, K, TOPK)
+    n = t["n_nodes"]
+    cand = np.concatenate([[0], rng.permutation(V)[:TOPK], rng.permutation(V)[:TOPK],
+                           rng.permutation(V)[:TOPK]]).astype(np.int32)[None, :]
+    hidden = rng.standard_normal((1, n, 4))
+    for target in itertools.product(range(V), repeat=n):
+        target = np.array(target, np.int32)[None, :]
+        res = AC.accept_batch(t, cand, target_ids=target)
+        carry = AC.frontier_carry(res, hidden)
+        walk = AC.tree_walk_accept(T.tree_tokens(t, cand[0]), target[0], t["parent"])
+        assert int(res["frontier_row"][0]) == walk[-1]
+        assert int(carry["next_root"][0]) == int(target[0][walk[-1]])
+        children = [v for v, par in enumerate(t["parent"]) if par == walk[-1]]
+        tokens = T.tree_tokens(t, cand[0])
+        assert all(int(tokens[c]) != int(carry["next_root"][0]) for c in children)
+        assert np.array_equal(carry["h_next"][0], hidden[0, walk[-1]])
+
+
+def test_frontier_carry_a31_trace():
+    """The A31 commit trace ([M7.2] §0x06B-§0x06C): tokens [11, 22, 31] on rows [0, 2, 6] are
+    published (a = 2) and the printed terminal frontier is row 6, so the next round starts
+    from row 6's distributions -- not row 2's (a - 1) nor another path's."""
+    g, t, tokens = a31()
+    commit = g["commit"]
+    target = np.full(t["n_nodes"], 999, np.int32)
+    target[0] = 22          # after the root the target wants 22 (row 2)
+    target[2] = 31          # after (11, 22) it wants 31 (row 6)
+    target[6] = 777         # the token the target emits after the accepted prefix
+    res = AC.accept_batch(t, np.array([[g["root_token"]] + g["head0_ranks"] + g["head1_ranks"]]),
+                          target_ids=target[None, :])
+    assert res["accepted_tokens"][0][: commit["G"]].tolist() == commit["tokens"]
+    assert int(res["frontier_row"][0]) == commit["terminal_frontier_row"] == 6
+    hidden = np.arange(t["n_nodes"] * 3, dtype=np.float64).reshape(1, t["n_nodes"], 3)
+    carry = AC.frontier_carry(res, hidden)
+    assert int(carry["next_root"][0]) == 777
+    assert np.array_equal(carry["h_next"][0], hidden[0, 6])
+
+
 # ---------------------------------------------------------------- typical acceptance
 
 def test_typical_five_token_distribution_all_pass():

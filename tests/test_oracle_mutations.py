@@ -162,6 +162,31 @@ def test_sentinel_as_index_is_caught(monkeypatch):
     must_fail(PA.test_sentinel_is_never_a_match)
 
 
+def test_frontier_from_row_a_minus_one_is_caught(monkeypatch):
+    real = AC.greedy_accept
+
+    def one_short(tokens, target, retrieve):
+        res = real(tokens, target, retrieve)
+        res["frontier_row"] = res["rows"][-2] if len(res["rows"]) > 1 else res["rows"][-1]
+        return res
+    monkeypatch.setattr(AC, "greedy_accept", one_short)
+    must_fail(PA.test_frontier_carry_a31_trace)
+    must_fail(PA.test_frontier_carry_is_where_the_tree_walk_stops, 0,
+              [(0,), (1,), (0, 0), (0, 1), (1, 0), (1, 1)])
+
+
+def test_frontier_from_another_path_is_caught(monkeypatch):
+    real = AC.greedy_accept
+
+    def other_path(tokens, target, retrieve):
+        res = real(tokens, target, retrieve)
+        alt = int(retrieve[(res["best_path"] + 1) % len(retrieve)][res["accept_len"]])
+        res["frontier_row"] = alt if alt >= 0 else res["frontier_row"]
+        return res
+    monkeypatch.setattr(AC, "greedy_accept", other_path)
+    must_fail(PA.test_frontier_carry_a31_trace)
+
+
 def test_typical_max_instead_of_min_is_caught(monkeypatch):
     monkeypatch.setattr(TY, "threshold", lambda p, epsilon=TY.EPSILON, alpha=TY.ALPHA:
                         max(epsilon, alpha * float(np.exp(-TY.entropy(p)))))
