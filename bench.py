@@ -5,9 +5,9 @@
 
 A step is one whole round over one batch of synthetic inputs already resident
 in HBM.  By default (``--round verify``) that is ``medusa_tree_attn`` (RoPE at P + depth, staged K/V rows, tree
-attention), ``medusa_accept`` (greedy acceptance over fp32 target logits) and
-``medusa_kv_compact`` (winning-path K/V gather), on one stream with no host
-synchronisation.  ``--round full`` runs the batched full round: the Medusa head
+attention) and ``medusa_accept_commit`` (greedy acceptance over fp32 target logits and the
+winning-path K/V gather in one call; ``--commit separate`` uses ``medusa_accept`` then
+``medusa_kv_compact``), on one stream with no host synchronisation.  ``--round full`` runs the batched full round: the Medusa head
 step ``medusa_head_candidates`` (W2 (SiLU(W1 h) + h) for four heads, top-10 of
 each, candidate rows written on the device) comes first in every step and
 fills the candidates that the acceptance reads.  The tree itself is compiled once on the host before the
@@ -231,6 +231,10 @@ def main():
                     help="override the workload's context length P (secondary runs, e.g. llama7b at 4096)")
     ap.add_argument("--accept", choices=["greedy", "typical"], default="greedy",
                     help="acceptance rule of the round (typical: temperature 1, epsilon 0.3, alpha 0.09)")
+    ap.add_argument("--commit", choices=["fused", "separate"], default="fused",
+                    help="greedy rounds: accept and compact in one call (fused) or two")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same number of steps replayed from one captured HIP graph")
     ap.add_argument("--round", choices=["verify", "full"], default="verify",
                     help="full: the Medusa head step fills the candidates first in every step")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for > 512 MB)")
@@ -294,61 +298,106 @@ def main():
     # reset copy inside the timed loop.  Argument tuples are built up front as well, so the
     # timed loop only calls into the library.
     total = args.warmup + args.steps
-    ctl = pristine.repeat(total, 1).contiguous()   # [steps][B + 1]
+    fused = args.accept == "greedy" and args.commit == "fused"
     kc_arrs = [(ctypes.c_void_p * 1)(s["kc"].data_ptr()) for s in sets]
     vc_arrs = [(ctypes.c_void_p * 1)(s["vc"].data_ptr()) for s in sets]
-    calls = []
-    for i in range(total):
-        s, kc_arr, vc_arr = sets[i % n_sets], kc_arrs[i % n_sets], vc_arrs[i % n_sets]
-        prefix, status = p(ctl[i]), p(ctl[i, w.B:])
-        attn = [sptr, dcode, w.B, w.Hq, w.Hkv, w.d, N, p(shared["depth"]), p(shared["mask"]),
-                tree["mask_words"], prefix, p(s["q"]), p(s["kn"]), p(s["vn"]), p(s["kc"]),
-                p(s["vc"]), x["S_max"], float(w.rope_base), p(s["out"]), p(s["attn_ws"]),
-                s["attn_ws"].numel(), status]
-        if args.accept == "typical":
-            acc = (sptr, w.B, N, w.vocab, p(s["logits"]), 1.0, 0.3, 0.09, p(s["cand"]),
-                   x["candidates"].shape[1], p(shared["tidx"]), p(shared["retrieve"]), nn, width,
-                   p(s["best"]), p(s["alen"]), p(s["tokens"]), p(s["frontier"]), p(s["acc_ws"]),
-                   s["acc_ws"].numel(), status, None, None)
-        else:
-            acc = (sptr, w.B, N, w.vocab if x["logits"] is not None else 0, p(s["logits"]), p(s["tids"]),
-                   p(s["cand"]), x["candidates"].shape[1], p(shared["tidx"]), p(shared["retrieve"]), nn,
-                   width, p(s["best"]), p(s["alen"]), p(s["tokens"]), p(s["frontier"]), p(s["acc_ws"]),
-                   s["acc_ws"].numel(), status, None, None)
-        cmp_ = (sptr, dcode, 1, w.B, w.Hkv, w.d, x["S_max"], N, ctypes.cast(kc_arr, ctypes.c_void_p),
-                ctypes.cast(vc_arr, ctypes.c_void_p), p(shared["retrieve"]), nn, width, p(s["best"]),
-                p(s["alen"]), prefix, status, None, None)
-        head = None
-        if heads is not None:
-            head = (sptr, w.B, w.num_heads, hidden, w.vocab, w.topk, p(heads["h"]), p(heads["W1"]),
-                    p(heads["W2"]), p(heads["root"]), p(s["cand"]), None, p(heads["ws"]),
-                    heads["ws"].numel(), status)
-        calls.append((attn, acc, cmp_, head))
+    hidden_rows = None
+    if heads is not None and fused:
+        # the tree rows' hidden states: the frontier carry feeds the next head step from them
+        hidden_rows = torch.randn((w.B, N, hidden), device="cuda").to(torch.bfloat16)
 
-    accept_fn = lib.medusa_accept_typical if args.accept == "typical" else lib.medusa_accept
+    def build_calls(sptr, ctl, n):
+        calls = []
+        for i in range(n):
+            s, kc_arr, vc_arr = sets[i % n_sets], kc_arrs[i % n_sets], vc_arrs[i % n_sets]
+            prefix, status = p(ctl[i]), p(ctl[i, w.B:])
+            attn = (sptr, dcode, w.B, w.Hq, w.Hkv, w.d, N, p(shared["depth"]), p(shared["mask"]),
+                    tree["mask_words"], prefix, p(s["q"]), p(s["kn"]), p(s["vn"]), p(s["kc"]),
+                    p(s["vc"]), x["S_max"], float(w.rope_base), p(s["out"]), p(s["attn_ws"]),
+                    s["attn_ws"].numel(), status)
+            V = w.vocab if x["logits"] is not None else 0
+            n_slots = x["candidates"].shape[1]
+            cmp_ = None
+            if args.accept == "typical":
+                acc = (sptr, w.B, N, w.vocab, p(s["logits"]), 1.0, 0.3, 0.09, p(s["cand"]), n_slots,
+                       p(shared["tidx"]), p(shared["retrieve"]), nn, width, p(s["best"]), p(s["alen"]),
+                       p(s["tokens"]), p(s["frontier"]), p(s["acc_ws"]), s["acc_ws"].numel(), status)
+            elif fused:
+                carry = ((hidden, p(hidden_rows), p(heads["h"]), p(heads["root"])) if hidden_rows is not None
+                         else (0, None, None, None))
+                acc = (sptr, w.B, N, V, p(s["logits"]), p(s["tids"]), p(s["cand"]), n_slots, p(shared["tidx"]),
+                       p(shared["retrieve"]), nn, width, p(s["best"]), p(s["alen"]), p(s["tokens"]),
+                       p(s["frontier"]), dcode, 1, w.Hkv, w.d, x["S_max"], ctypes.cast(kc_arr, ctypes.c_void_p),
+                       ctypes.cast(vc_arr, ctypes.c_void_p), prefix) + carry + (
+                           p(s["acc_ws"]), s["acc_ws"].numel(), status)
+            else:
+                acc = (sptr, w.B, N, V, p(s["logits"]), p(s["tids"]), p(s["cand"]), n_slots, p(shared["tidx"]),
+                       p(shared["retrieve"]), nn, width, p(s["best"]), p(s["alen"]), p(s["tokens"]),
+                       p(s["frontier"]), p(s["acc_ws"]), s["acc_ws"].numel(), status)
+                cmp_ = (sptr, dcode, 1, w.B, w.Hkv, w.d, x["S_max"], N, ctypes.cast(kc_arr, ctypes.c_void_p),
+                        ctypes.cast(vc_arr, ctypes.c_void_p), p(shared["retrieve"]), nn, width, p(s["best"]),
+                        p(s["alen"]), prefix, status)
+            head = None
+            if heads is not None:
+                head = (sptr, w.B, w.num_heads, hidden, w.vocab, w.topk, p(heads["h"]), p(heads["W1"]),
+                        p(heads["W2"]), p(heads["root"]), p(s["cand"]), None, p(heads["ws"]),
+                        heads["ws"].numel(), status)
+            calls.append((attn, acc, cmp_, head))
+        return calls
+
+    accept_fn = (lib.medusa_accept_typical if args.accept == "typical"
+                 else lib.medusa_accept_commit if fused else lib.medusa_accept)
     ev = HipEvents()
     events = [(ev.create(), ev.create()) for _ in range(total)]
     head_events = [(ev.create(), ev.create()) for _ in range(total)] if heads is not None else []
+    no_events = (None, None)
 
-    def step(i):
-        attn, acc, cmp_, head = calls[i]
+    def step(call, evs, hevs):
+        attn, acc, cmp_, head = call
         rc = 0
         if head is not None:
-            rc |= lib.medusa_head_candidates(*head, head_events[i][0], head_events[i][1])
-        rc |= lib.medusa_tree_attn(*attn, events[i][0], events[i][1])
-        rc |= accept_fn(*acc)
-        rc |= lib.medusa_kv_compact(*cmp_)
+            rc |= lib.medusa_head_candidates(*head, *hevs)
+        rc |= lib.medusa_tree_attn(*attn, *evs)
+        rc |= accept_fn(*acc, None, None)
+        if cmp_ is not None:
+            rc |= lib.medusa_kv_compact(*cmp_, None, None)
         if rc:
-            raise RuntimeError(f"library call failed at step {i}")
+            raise RuntimeError("library call failed")
 
+    ctl = pristine.repeat(total, 1).contiguous()   # [steps][B + 1]
+    calls = build_calls(sptr, ctl, total)
+    hev = lambda i: head_events[i] if head_events else no_events
     for i in range(args.warmup):
-        step(i)
+        step(calls[i], events[i], hev(i))
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.warmup, total):
-        step(i)
+        step(calls[i], events[i], hev(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+
+    graph_info = None
+    if args.graph:
+        # the same number of steps, captured once on a stream of their own (no timing
+        # events) and replayed as one graph, with fresh control blocks
+        ctl_g = pristine.repeat(args.steps, 1).contiguous()
+        cap = torch.cuda.Stream()
+        gcalls = build_calls(cap.cuda_stream, ctl_g, args.steps)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for c in gcalls:
+                step(c, no_events, no_events)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        g_el = time.perf_counter() - t0
+        g_status = ctl_g[:, w.B].cpu().numpy()
+        if g_status.any():
+            raise RuntimeError(f"graph replay status words {sorted(set(g_status.tolist()))}")
+        graph_info = {"ms_per_step": g_el / args.steps * 1e3, "value": w.B * N * args.steps / g_el,
+                      "library_calls_per_step": (3 if heads is not None else 2) + (0 if fused else 1)}
+        log(f"[bench] graph replay: {g_el / args.steps * 1e6:.1f} us per step")
 
     statuses = ctl[:, w.B].cpu().numpy()
     if statuses.any():
@@ -385,7 +434,8 @@ def main():
         "config": {"workload": (f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d_h={w.d}, P={w.P}, "
                                 f"N={N} ({w.tree} tree), V={w.vocab}"),
                    "global_batch": w.B, "seq_len": w.P, "tree_nodes": N, "buffer_sets": n_sets,
-                   "accept": args.accept, "round": args.round},
+                   "accept": args.accept, "round": args.round,
+                   "commit": "fused" if fused else "separate"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(src_hash),
                      "kernel": "medusa_tree_attn", "algorithmic_bytes": alg,
@@ -415,6 +465,8 @@ def main():
         result["config"]["workload"] += f"; head step K={w.num_heads}, hidden={hidden}, topk={w.topk}"
         log(f"[bench] head step mean {h_mean * 1e6:.2f} us -> {h_ach:.0f} GB/s "
             f"({h_ach / HBM_PEAK_GBS:.1%} of HBM peak, {h_ach / stream_gbs:.1%} of the read stream)")
+    if graph_info:
+        result["graph"] = graph_info
     if copy_info:
         result["copy_calibration"] = copy_info
     log(f"[bench] attention mean {mean_s * 1e6:.2f} us -> {achieved:.0f} GB/s "

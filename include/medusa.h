@@ -6,6 +6,11 @@
  *   medusa_tree_attn     device: RoPE at P+depth, staged K/V rows, tree attention
  *   medusa_accept        device: greedy longest-prefix acceptance
  *   medusa_kv_compact    device: gather the winning path's K/V rows into the cache
+ * and, around them:
+ *   medusa_accept_typical   device: typical acceptance instead of greedy
+ *   medusa_accept_commit    device: greedy acceptance, compaction and the frontier carry
+ *                           in one call
+ *   medusa_head_candidates  device: the Medusa heads' top-k candidate rows
  *
  * Pages cited (by title and section):
  *   [M7.2]  "M7.2 - Medusa: Multi-Head Candidates, Tree Attention, and Verification"
@@ -234,6 +239,45 @@ medusa_status medusa_accept_typical(void* stream, int32_t B, int32_t N, int32_t 
                                     int32_t* accept_len, int32_t* accepted_tokens,
                                     int32_t* frontier_row, void* workspace, size_t workspace_bytes,
                                     int32_t* d_status, void* ev_start, void* ev_stop);
+
+/* ------------------------------------------------------------------ accept, commit, carry
+ *
+ * Greedy acceptance (exactly as medusa_accept, same outputs), then, per sequence and with
+ * the chosen path, the compaction of medusa_kv_compact ([M7.2] §0x06A-§0x06B: for j < G_b
+ * = accept_len[b] + 1, cache rows P_b + j <- P_b + retrieve[best][j] of every layer, kv
+ * head, K and V, all source rows read before any is written; then prefix_len[b] += G_b)
+ * and the frontier carry ([M7.2] §0x06C: the next round starts from the terminal row
+ * f_b = frontier_row[b]):
+ *   next_root[b]  = the target token of row f_b (argmax of logits[b][f_b], lowest index on
+ *                   ties; target_ids[b][f_b] when target ids are given)   (optional)
+ *   h_next[b][:]  = hidden[b][f_b][:]                                     (optional)
+ * One call replaces medusa_accept + medusa_kv_compact and launches two kernels.  Nothing in
+ * it allocates, copies through the host or synchronises, so a round built from it can be
+ * captured in a HIP graph and replayed ([Chai] "把 Python 控制流赶出热路径").
+ * Arguments as medusa_accept and medusa_kv_compact (k_cache / v_cache: host arrays of
+ * n_layers device pointers, each [B][Hkv][S_max][d_h] of dtype dt, 16-byte aligned;
+ * d_prefix_len int32 [B] device, in: P_b, out: P_b + G_b), plus:
+ *   hidden     device [B][N][hidden_dim] of dtype dt (the tree rows' hidden states), or NULL
+ *   h_next     device [B][hidden_dim] of dtype dt, or NULL (together with hidden)
+ *   next_root  device int32 [B], or NULL
+ * Limits: n_layers <= 32, path_width <= 8, d_h * size(dt) and hidden_dim * size(dt)
+ * multiples of 16 bytes (else MEDUSA_EUNSUPPORTED).  The copy runs in one workgroup per
+ * sequence: with many layers and few sequences medusa_kv_compact spreads it wider.
+ * Workspace: medusa_accept_workspace_size(B, N) bytes when logits are given.
+ * Device-detected errors (d_status), all before any store of the call: those of
+ * medusa_accept, and P_b < 0 or P_b + N > S_max for any sequence -> MEDUSA_ECAPACITY.
+ */
+medusa_status medusa_accept_commit(void* stream, int32_t B, int32_t N, int32_t V, const float* logits,
+                                   const int32_t* target_ids, const int32_t* candidates, int32_t n_slots,
+                                   const int32_t* d_tree_indices, const int32_t* d_retrieve,
+                                   int32_t n_paths, int32_t path_width, int32_t* best_path,
+                                   int32_t* accept_len, int32_t* accepted_tokens, int32_t* frontier_row,
+                                   medusa_dtype dt, int32_t n_layers, int32_t Hkv, int32_t d_h,
+                                   int32_t S_max, void* const* k_cache, void* const* v_cache,
+                                   int32_t* d_prefix_len, int32_t hidden_dim, const void* hidden,
+                                   void* h_next, int32_t* next_root, void* workspace,
+                                   size_t workspace_bytes, int32_t* d_status, void* ev_start,
+                                   void* ev_stop);
 
 /* ------------------------------------------------------------------ head step and candidates
  *

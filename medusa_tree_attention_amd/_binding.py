@@ -64,6 +64,9 @@ _SIGNATURES = {
                                       _SZ, _P, _P, _P]),
     "medusa_kv_compact": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32,
                                  _I32, _P, _P, _P, _P, _P, _P]),
+    "medusa_accept_commit": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P,
+                                    _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P,
+                                    _P, _P, _P, _SZ, _P, _P, _P]),
 }
 
 
@@ -214,6 +217,33 @@ def medusa_accept_typical(candidates, tree_indices, retrieve, best_path, accept_
         _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _ptr(status), ev_start, ev_stop)
     _check("medusa_accept_typical", code)
+
+
+def medusa_accept_commit(candidates, tree_indices, retrieve, best_path, accept_len, accepted_tokens,
+                         frontier_row, k_caches, v_caches, prefix_len, status, logits=None,
+                         target_ids=None, workspace=None, hidden=None, h_next=None, next_root=None,
+                         stream=None, ev_start=None, ev_stop=None):
+    """Greedy acceptance, compaction of every layer in ``k_caches``/``v_caches`` (lists of
+    [B,Hkv,S_max,d] tensors) and the frontier carry (``hidden`` [B,N,H] -> ``h_next`` [B,H],
+    ``next_root`` [B]) in one call."""
+    B, n_slots = candidates.shape
+    N = tree_indices.shape[0]
+    V = logits.shape[2] if logits is not None else 0
+    n_paths, width = retrieve.shape
+    n_layers = len(k_caches)
+    _, Hkv, S_max, d = k_caches[0].shape
+    karr = (ctypes.c_void_p * max(n_layers, 1))(*[_ptr(t) for t in k_caches])
+    varr = (ctypes.c_void_p * max(n_layers, 1))(*[_ptr(t) for t in v_caches])
+    hidden_dim = hidden.shape[-1] if hidden is not None else 0
+    code = load().medusa_accept_commit(
+        _stream(stream), B, N, V, _ptr(logits), _ptr(target_ids), _ptr(candidates), n_slots,
+        _ptr(tree_indices), _ptr(retrieve), n_paths, width, _ptr(best_path), _ptr(accept_len),
+        _ptr(accepted_tokens), _ptr(frontier_row), _dtype_code(k_caches[0]), n_layers, Hkv, d, S_max,
+        ctypes.cast(karr, ctypes.c_void_p), ctypes.cast(varr, ctypes.c_void_p), _ptr(prefix_len),
+        hidden_dim, _ptr(hidden), _ptr(h_next), _ptr(next_root), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _ptr(status), ev_start, ev_stop)
+    _check("medusa_accept_commit", code)
 
 
 # ------------------------------------------------------------------ head step

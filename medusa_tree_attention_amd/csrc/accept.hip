@@ -27,6 +27,16 @@
 //                    guarded entropy over them: the row is read from HBM once.
 // Kernel 2 (select):  as above, with the typical edge test and the log-likelihood
 //                     tie-break.
+//
+// Accept and commit in one pass (medusa_accept_commit): the greedy select kernel's block
+// for sequence b goes on, once it has chosen the path, to compact that sequence's K/V rows
+// ([M7.2] §0x06A-§0x06B: cache rows P + j <- P + retrieve[p*][j] for j < G, every layer,
+// kv head and matrix) and to hand the next round its starting state ([M7.2] §0x06C: the
+// target's token at the terminal row is the next root, and the hidden state of that row
+// feeds the next head step).  A thread owns one 16-byte column of one (layer, head,
+// matrix) and reads it from all G source rows before writing any destination row, which
+// is the snapshot [M7.2] §0x06B asks for (columns are disjoint bytes); only this block
+// touches sequence b's rows and length, so no ordering crosses blocks.
 
 #include <algorithm>
 #include <cmath>
@@ -35,6 +45,9 @@
 #include "common.h"
 
 namespace medusa {
+
+constexpr int kCommitLayers = 32;  // layers one accept-and-commit call compacts
+constexpr int kCommitWidth = 8;    // path width (K + 1) the commit handles in registers
 
 struct AcceptArgs {
   const float* logits;        // [B][N][V] or null
@@ -52,7 +65,34 @@ struct AcceptArgs {
   int32_t B, N, V, n_slots, n_paths, W;
   int32_t parts, chunk4;      // pieces per row; float4 columns per piece (vector path)
   float inv_temperature, epsilon, alpha;  // typical: inv_temperature = log2(e) / T
+  // accept and commit
+  void* kc[kCommitLayers];    // per layer: cache [B][Hkv][S_max][row_bytes]
+  void* vc[kCommitLayers];
+  int32_t* prefix_len;        // [B], advanced by G
+  const unsigned char* hidden;  // [B][N][hidden_bytes] or null
+  unsigned char* h_next;      // [B][hidden_bytes] or null
+  int32_t* next_root;         // [B] or null
+  int32_t n_layers, Hkv, S_max, row_bytes, hidden_bytes;
+  int32_t check_capacity;     // the argmax kernel checks P_b + N <= S_max for every b
 };
+
+// Every sequence's staged block [P_b, P_b + N) must lie inside the cache, checked before
+// any block of the select kernel advances a length (a block that checked afterwards could
+// see an advanced length): by the first block of the kernel that runs before it.
+__device__ __forceinline__ void check_capacity(const AcceptArgs& a, bool failed) {
+  if (threadIdx.x >= 64) return;
+  bool bad = false;
+  for (int i = threadIdx.x; i < a.B; i += 64) {
+    const int64_t P = a.prefix_len[i];
+    bad = bad || P < 0 || P + a.N > a.S_max;
+  }
+  if (__ballot(bad) && threadIdx.x == 0 && !failed) raise_status(a.status, MEDUSA_ECAPACITY);
+}
+
+// the capacity check alone, for target-id rounds (which have no argmax kernel)
+__global__ __launch_bounds__(64) void capacity_kernel(AcceptArgs a) {
+  check_capacity(a, round_failed(a.status));
+}
 
 __device__ __forceinline__ void keep_better(float& v, int& i, float ov, int oi) {
   if (ov > v || (ov == v && oi < i)) {
@@ -69,6 +109,7 @@ constexpr size_t kSelectLds = 65536;  // bytes of tree buffers, candidates and t
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(AcceptArgs a) {
   // the status gates the stores only: its load overlaps the logits stream
   const bool failed = round_failed(a.status);
+  if (a.check_capacity && blockIdx.x == 0) check_capacity(a, failed);
   const int64_t r = blockIdx.x / a.parts;
   const int piece = int(blockIdx.x % a.parts);
   const float* row = a.logits + r * a.V;
@@ -266,7 +307,7 @@ __device__ __forceinline__ int32_t row_target(const AcceptArgs& a, int b, int u)
 // buffers and reach the same verdict.  kTypical selects the typical edge test (candidate
 // ids must then be tokens of the vocabulary: they index the logits) and ranks paths of
 // equal length by their summed log p.
-template <bool kStaged, bool kTypical>
+template <bool kStaged, bool kTypical, bool kCommit = false>
 __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
   const bool failed = round_failed(a.status);  // gates the stores only
   const int b = blockIdx.x;
@@ -384,6 +425,45 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
     a.accept_len[b] = alen;
     a.frontier[b] = r[alen];
   }
+  if (kCommit) {
+    const int64_t P = a.prefix_len[b];  // only this block writes it, after the reads below
+    const int G = alen + 1;
+    int32_t src[kCommitWidth];
+#pragma unroll
+    for (int j = 0; j < kCommitWidth; ++j) src[j] = r[j < G ? j : 0];
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int cpr = a.row_bytes >> 4;  // 16-byte columns per row
+    const int per_layer = a.Hkv * 2 * cpr;
+    const int items = a.n_layers * per_layer;
+    // column it of (layer, kv head, matrix): all G source rows are read before any
+    // destination row is written (the rows past G re-read row r[0] and are not stored)
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+      const int l = it / per_layer, rem = it - l * per_layer;
+      const int g = rem / (2 * cpr), rem2 = rem - g * 2 * cpr;
+      const int m = rem2 / cpr, c = rem2 - m * cpr;
+      unsigned char* base = static_cast<unsigned char*>(m ? a.vc[l] : a.kc[l]) +
+                            ((int64_t(b) * a.Hkv + g) * a.S_max + P) * a.row_bytes + 16 * c;
+      u32x4 v[kCommitWidth];
+#pragma unroll
+      for (int j = 0; j < kCommitWidth; ++j)
+        v[j] = *reinterpret_cast<const u32x4*>(base + int64_t(src[j]) * a.row_bytes);
+#pragma unroll
+      for (int j = 0; j < kCommitWidth; ++j)
+        if (j < G) *reinterpret_cast<u32x4*>(base + int64_t(j) * a.row_bytes) = v[j];
+    }
+    const int fr = r[alen];
+    if (a.h_next) {  // the hidden state of the terminal row
+      const unsigned char* hs = a.hidden + (int64_t(b) * a.N + fr) * a.hidden_bytes;
+      unsigned char* hd = a.h_next + int64_t(b) * a.hidden_bytes;
+      for (int i = threadIdx.x; i < (a.hidden_bytes >> 4); i += blockDim.x)
+        *reinterpret_cast<u32x4*>(hd + 16 * i) = *reinterpret_cast<const u32x4*>(hs + 16 * i);
+    }
+    __syncthreads();  // every thread has read P
+    if (threadIdx.x == 0) {
+      if (a.next_root) a.next_root[b] = tgt(fr);
+      a.prefix_len[b] = int32_t(P + G);
+    }
+  }
 }
 
 }  // namespace medusa
@@ -455,6 +535,95 @@ extern "C" medusa_status medusa_accept(void* stream, int32_t B, int32_t N, int32
   const void* sel = staged ? reinterpret_cast<const void*>(&select_kernel<true, false>)
                            : reinterpret_cast<const void*>(&select_kernel<false, false>);
   return launch(sel, dim3(B), dim3(256), staged ? lds : 0, s, a, ev_start, ev_stop);
+}
+
+extern "C" medusa_status medusa_accept_commit(
+    void* stream, int32_t B, int32_t N, int32_t V, const float* logits, const int32_t* target_ids,
+    const int32_t* candidates, int32_t n_slots, const int32_t* d_tree_indices, const int32_t* d_retrieve,
+    int32_t n_paths, int32_t path_width, int32_t* best_path, int32_t* accept_len, int32_t* accepted_tokens,
+    int32_t* frontier_row, medusa_dtype dt, int32_t n_layers, int32_t Hkv, int32_t d_h, int32_t S_max,
+    void* const* k_cache, void* const* v_cache, int32_t* d_prefix_len, int32_t hidden_dim,
+    const void* hidden, void* h_next, int32_t* next_root, void* workspace, size_t workspace_bytes,
+    int32_t* d_status, void* ev_start, void* ev_stop) {
+  if (B < 1 || N < 1 || n_slots < 1 || n_paths < 1 || path_width < 1) return MEDUSA_EINVAL;
+  if ((logits == nullptr) == (target_ids == nullptr)) return MEDUSA_EINVAL;
+  if (logits != nullptr && V < 1) return MEDUSA_EINVAL;
+  if (!candidates || !d_tree_indices || !d_retrieve || !best_path || !accept_len || !accepted_tokens ||
+      !frontier_row || !d_status || !d_prefix_len)
+    return MEDUSA_EINVAL;
+  if (dt != MEDUSA_F32 && dt != MEDUSA_BF16) return MEDUSA_EINVAL;
+  if (n_layers < 0 || Hkv < 1 || S_max < N || hidden_dim < 0) return MEDUSA_EINVAL;
+  if (n_layers > 0 && (!k_cache || !v_cache)) return MEDUSA_EINVAL;
+  for (int32_t l = 0; l < n_layers; ++l)
+    if (!k_cache[l] || !v_cache[l]) return MEDUSA_EINVAL;
+  if ((h_next == nullptr) != (hidden == nullptr) || (h_next != nullptr && hidden_dim < 1)) return MEDUSA_EINVAL;
+  const int32_t esize = dt == MEDUSA_BF16 ? 2 : 4;
+  const int64_t row_bytes = int64_t(d_h) * esize, hidden_bytes = int64_t(hidden_dim) * esize;
+  if (d_h < 1 || row_bytes % 16 != 0 || (h_next != nullptr && hidden_bytes % 16 != 0)) return MEDUSA_EUNSUPPORTED;
+  if (n_layers > kCommitLayers || path_width > kCommitWidth) return MEDUSA_EUNSUPPORTED;
+  for (int32_t l = 0; l < n_layers; ++l)
+    if (((reinterpret_cast<uintptr_t>(k_cache[l]) | reinterpret_cast<uintptr_t>(v_cache[l])) & 15) != 0)
+      return MEDUSA_EINVAL;
+  if (h_next != nullptr &&
+      ((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(h_next)) & 15) != 0)
+    return MEDUSA_EINVAL;
+  if (logits != nullptr &&
+      (workspace == nullptr || workspace_bytes < medusa_accept_workspace_size(B, N)))
+    return MEDUSA_EBUFSIZE;
+
+  AcceptArgs a{};
+  a.logits = logits;
+  a.target_ids = target_ids;
+  a.candidates = candidates;
+  a.tree_indices = d_tree_indices;
+  a.retrieve = d_retrieve;
+  a.best_path = best_path;
+  a.accept_len = accept_len;
+  a.accepted = accepted_tokens;
+  a.frontier = frontier_row;
+  a.part = static_cast<int2*>(workspace);
+  a.status = d_status;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.n_slots = n_slots;
+  a.n_paths = n_paths;
+  a.W = path_width;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    a.kc[l] = k_cache[l];
+    a.vc[l] = v_cache[l];
+  }
+  a.prefix_len = d_prefix_len;
+  a.hidden = static_cast<const unsigned char*>(hidden);
+  a.h_next = static_cast<unsigned char*>(h_next);
+  a.next_root = next_root;
+  a.n_layers = n_layers;
+  a.Hkv = Hkv;
+  a.S_max = S_max;
+  a.row_bytes = int32_t(row_bytes);
+  a.hidden_bytes = int32_t(hidden_bytes);
+  a.check_capacity = 1;
+  const int64_t rows = int64_t(B) * N;
+  const int64_t n4 = (int64_t(V) + 3) / 4;
+  const int64_t min_piece = 2 * kArgmaxThreads;
+  int64_t parts = std::min<int64_t>({int64_t(kMaxParts), std::max<int64_t>(1, 1024 / rows),
+                                     std::max<int64_t>(1, n4 / min_piece)});
+  a.parts = int32_t(std::max<int64_t>(1, parts));
+  a.chunk4 = int32_t((n4 + a.parts - 1) / a.parts);
+  const size_t lds = (2 * size_t(N) + size_t(n_slots) + size_t(n_paths) * path_width) * sizeof(int32_t);
+  const bool staged = lds <= kSelectLds;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the capacity of every sequence is checked by a kernel that completes before the select
+  // kernel advances any length: the argmax kernel, or a one-wave kernel for target ids
+  medusa_status st = logits != nullptr
+                         ? launch(reinterpret_cast<const void*>(&argmax_kernel), dim3(unsigned(rows * a.parts)),
+                                  dim3(kArgmaxThreads), 0, s, a, ev_start, nullptr)
+                         : launch(reinterpret_cast<const void*>(&capacity_kernel), dim3(1), dim3(64), 0, s, a,
+                                  ev_start, nullptr);
+  if (st != MEDUSA_OK) return st;
+  const void* sel = staged ? reinterpret_cast<const void*>(&select_kernel<true, false, true>)
+                           : reinterpret_cast<const void*>(&select_kernel<false, false, true>);
+  return launch(sel, dim3(B), dim3(256), staged ? lds : 0, s, a, nullptr, ev_stop);
 }
 
 extern "C" medusa_status medusa_accept_typical(void* stream, int32_t B, int32_t N, int32_t V,

@@ -51,9 +51,13 @@ template <typename Args>
 inline medusa_status launch(const void* kernel, dim3 grid, dim3 block, size_t shmem,
                             hipStream_t stream, Args& args, void* ev_start, void* ev_stop) {
   void* kargs[] = {&args};
-  hipError_t e = hipExtLaunchKernel(kernel, grid, block, kargs, shmem, stream,
-                                    static_cast<hipEvent_t>(ev_start),
-                                    static_cast<hipEvent_t>(ev_stop), 0);
+  // without timing events the plain launch (what stream capture records as a kernel node);
+  // with them, the extended launch that records the events from the dispatch itself
+  const hipError_t e =
+      ev_start == nullptr && ev_stop == nullptr
+          ? hipLaunchKernel(kernel, grid, block, kargs, shmem, stream)
+          : hipExtLaunchKernel(kernel, grid, block, kargs, shmem, stream, static_cast<hipEvent_t>(ev_start),
+                               static_cast<hipEvent_t>(ev_stop), 0);
   return e == hipSuccess ? MEDUSA_OK : MEDUSA_EHIP;
 }
 

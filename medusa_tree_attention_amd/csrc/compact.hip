@@ -269,9 +269,12 @@ extern "C" medusa_status medusa_kv_compact(void* stream, medusa_dtype dt, int32_
       a.v[i] = v_cache[i];
     }
     void* kargs[] = {&a, &n_layers};
-    const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(&compact_fused_kernel), dim3(1),
-                                            dim3(kFusedThreads), kargs, 0, s, static_cast<hipEvent_t>(ev_start),
-                                            static_cast<hipEvent_t>(ev_stop), 0);
+    const void* kern = reinterpret_cast<const void*>(&compact_fused_kernel);
+    const hipError_t e =
+        ev_start == nullptr && ev_stop == nullptr
+            ? hipLaunchKernel(kern, dim3(1), dim3(kFusedThreads), kargs, 0, s)
+            : hipExtLaunchKernel(kern, dim3(1), dim3(kFusedThreads), kargs, 0, s, static_cast<hipEvent_t>(ev_start),
+                                 static_cast<hipEvent_t>(ev_stop), 0);
     return e == hipSuccess ? MEDUSA_OK : MEDUSA_EHIP;
   }
   for (int32_t l0 = 0; l0 < n_layers; l0 += kLayersPerLaunch) {
