@@ -166,16 +166,17 @@ def cpu_model():
     return platform.machine()
 
 
-def stream_read_gbs(torch):
-    """STREAM-style read bandwidth of this GPU: a sum over 1 GiB of fp32 (four times the
-    Infinity Cache), timed with events on torch's stream, where the reduction runs."""
+def read_ceiling_gbs(torch, M):
+    """Practical read bandwidth of this GPU: the library's streaming-read probe over 1 GiB
+    (four times the Infinity Cache), timed with events on torch's stream, where it runs."""
     x = torch.ones(2 ** 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(M.medusa_read_probe_sink_size() // 4, dtype=torch.int32, device="cuda")
     for _ in range(3):
-        x.sum()
+        M.medusa_read_probe(x, sink)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(10):
-        x.sum()
+        M.medusa_read_probe(x, sink)
     e1.record()
     e1.synchronize()
     sec = e0.elapsed_time(e1) / 10 * 1e-3
@@ -417,7 +418,7 @@ def main():
         torch.cuda.synchronize()
         copy_info = "torch.neg over 2^26 fp32 (256 MiB read + 256 MiB written) x5"
 
-    stream_gbs = stream_read_gbs(torch)
+    ceiling_gbs = read_ceiling_gbs(torch, M)
     esize = 2 if w.dtype == "bf16" else 4
     alg = algorithmic_bytes(w, N, esize)
     mean_s = float(attn_ms.mean()) * 1e-3
@@ -443,7 +444,7 @@ def main():
                      "p10_us": float(np.percentile(attn_ms, 10)) * 1e3,
                      "p90_us": float(np.percentile(attn_ms, 90)) * 1e3,
                      "source_hash": src_hash,
-                     "stream_read_gbs": stream_gbs, "frac_of_stream_read": achieved / stream_gbs},
+                     "read_ceiling_gbs": ceiling_gbs, "frac_of_read_ceiling": achieved / ceiling_gbs},
         "attention_nodes_per_s": w.B * N / mean_s,
         "tree_compile_us": compile_us,
     }
@@ -460,18 +461,18 @@ def main():
             "mean_us": h_mean * 1e6, "median_us": float(np.median(head_ms)) * 1e3,
             "p10_us": float(np.percentile(head_ms, 10)) * 1e3,
             "p90_us": float(np.percentile(head_ms, 90)) * 1e3,
-            "source_hash": h_hash, "stream_read_gbs": stream_gbs,
-            "frac_of_stream_read": h_ach / stream_gbs}
+            "source_hash": h_hash, "read_ceiling_gbs": ceiling_gbs,
+            "frac_of_read_ceiling": h_ach / ceiling_gbs}
         result["config"]["workload"] += f"; head step K={w.num_heads}, hidden={hidden}, topk={w.topk}"
         log(f"[bench] head step mean {h_mean * 1e6:.2f} us -> {h_ach:.0f} GB/s "
-            f"({h_ach / HBM_PEAK_GBS:.1%} of HBM peak, {h_ach / stream_gbs:.1%} of the read stream)")
+            f"({h_ach / HBM_PEAK_GBS:.1%} of HBM peak, {h_ach / ceiling_gbs:.1%} of the read ceiling)")
     if graph_info:
         result["graph"] = graph_info
     if copy_info:
         result["copy_calibration"] = copy_info
     log(f"[bench] attention mean {mean_s * 1e6:.2f} us -> {achieved:.0f} GB/s "
-        f"({achieved / HBM_PEAK_GBS:.1%} of HBM peak, {achieved / stream_gbs:.1%} of the "
-        f"{stream_gbs:.0f} GB/s read stream); step {elapsed / args.steps * 1e6:.1f} us")
+        f"({achieved / HBM_PEAK_GBS:.1%} of HBM peak, {achieved / ceiling_gbs:.1%} of the "
+        f"{ceiling_gbs:.0f} GB/s read ceiling); step {elapsed / args.steps * 1e6:.1f} us")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on one round ...")
         result["cpu_baseline"] = cpu_baseline(w, x, xh)

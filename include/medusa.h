@@ -338,6 +338,20 @@ medusa_status medusa_kv_compact(void* stream, medusa_dtype dt, int32_t n_layers,
                                 int32_t* d_prefix_len, int32_t* d_status, void* ev_start,
                                 void* ev_stop);
 
+/* ------------------------------------------------------------------ measurement utility
+ *
+ * Not a step of the round: a streaming read of `bytes` (a multiple of 16) of device memory at
+ * `src` (16-byte aligned), every thread keeping eight 16-byte loads in flight, with one word
+ * per workgroup stored to `sink` (device, medusa_read_probe_sink_size() bytes).  Timed on a
+ * buffer larger than the 256 MB Infinity Cache it gives the practical read bandwidth of the
+ * chip, against which the round's memory-bound kernels are compared.
+ * Host errors: MEDUSA_EINVAL (NULL pointer, size or alignment).
+ */
+size_t medusa_read_probe_sink_size(void);
+
+medusa_status medusa_read_probe(void* stream, const void* src, size_t bytes, uint32_t* sink,
+                                void* ev_start, void* ev_stop);
+
 #ifdef __cplusplus
 }
 #endif

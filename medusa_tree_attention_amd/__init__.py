@@ -13,5 +13,6 @@ from ._binding import (  # noqa: F401
     BF16, F32, LIBRARY, MedusaError, STATUS, load, medusa_accept, medusa_accept_commit,
     medusa_accept_typical,
     medusa_accept_workspace_size, medusa_head_candidates, medusa_head_workspace_size,
-    medusa_kv_compact, medusa_tree_attn, medusa_tree_attn_workspace_size, medusa_tree_compile,
+    medusa_kv_compact, medusa_read_probe, medusa_read_probe_sink_size, medusa_tree_attn,
+    medusa_tree_attn_workspace_size, medusa_tree_compile,
 )

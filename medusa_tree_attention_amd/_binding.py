@@ -64,6 +64,8 @@ _SIGNATURES = {
                                       _SZ, _P, _P, _P]),
     "medusa_kv_compact": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32,
                                  _I32, _P, _P, _P, _P, _P, _P]),
+    "medusa_read_probe_sink_size": (_SZ, []),
+    "medusa_read_probe": (_I32, [_P, _P, _SZ, _P, _P, _P]),
     "medusa_accept_commit": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P,
                                     _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P,
                                     _P, _P, _P, _SZ, _P, _P, _P]),
@@ -280,3 +282,16 @@ def medusa_kv_compact(k_caches, v_caches, retrieve, best_path, accept_len, prefi
         n_paths, width, _ptr(best_path), _ptr(accept_len), _ptr(prefix_len), _ptr(status),
         ev_start, ev_stop)
     _check("medusa_kv_compact", code)
+
+
+# ------------------------------------------------------------------ measurement utility
+
+def medusa_read_probe_sink_size():
+    return int(load().medusa_read_probe_sink_size())
+
+
+def medusa_read_probe(src, sink, stream=None, ev_start=None, ev_stop=None):
+    """Stream ``src`` (a contiguous device tensor) once; ``sink`` receives one word per workgroup."""
+    code = load().medusa_read_probe(_stream(stream), _ptr(src), src.numel() * src.element_size(),
+                                    _ptr(sink), ev_start, ev_stop)
+    _check("medusa_read_probe", code)

@@ -13,7 +13,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmedusa.so")
 INCLUDE = os.path.join(ROOT, "include")
 
-HIP_SOURCES = ["attn.hip", "attn_mfma.hip", "accept.hip", "compact.hip", "heads.hip"]
+HIP_SOURCES = ["attn.hip", "attn_mfma.hip", "accept.hip", "compact.hip", "heads.hip", "probe.hip"]
 CPP_SOURCES = ["tree_compile.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
