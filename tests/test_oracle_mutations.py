@@ -10,11 +10,13 @@ import pytest
 
 import test_oracle_accept as PA
 import test_oracle_attention as PT
+import test_oracle_budget as PB
 import test_oracle_compact as PC
 import test_oracle_heads as PH
 import test_oracle_tree as PR
 from oracle import accept as AC
 from oracle import attention as A
+from oracle import budget as BU
 from oracle import compact as C
 from oracle import heads as HD
 from oracle import tree as T
@@ -185,6 +187,18 @@ def test_frontier_from_another_path_is_caught(monkeypatch):
         return res
     monkeypatch.setattr(AC, "greedy_accept", other_path)
     must_fail(PA.test_frontier_carry_a31_trace)
+
+
+def test_budget_by_accepted_length_alone_is_caught(monkeypatch):
+    """[M7.2] §0x04C: maximising E[A] per round is not maximising tokens per second."""
+    monkeypatch.setattr(BU, "cost", lambda nodes, us, n: 1.0)
+    must_fail(PB.test_hand_computed_four_node_case)
+
+
+def test_budget_without_the_fixed_cost_is_caught(monkeypatch):
+    real = BU.tree_budget
+    monkeypatch.setattr(BU, "tree_budget", lambda a, nodes, us, fixed, layers: real(a, nodes, us, 0.0, layers))
+    must_fail(PB.test_hand_computed_four_node_case)
 
 
 def test_typical_max_instead_of_min_is_caught(monkeypatch):
