@@ -222,6 +222,83 @@ def cpu_baseline(w, x, xh=None):
                        f"compaction; {dt:.1f} s on 1 thread of {cpu_model()}")}
 
 
+def budget_sweep(args, np, torch, M, workloads):
+    """Per-layer attention cost of the greedy trees T_N at several contexts P, and the node
+    budget medusa_tree_budget picks from it for each P.  The per-round fixed cost is the
+    backbone weight stream (--backbone-gb) at the read ceiling measured in the same run."""
+    import dataclasses
+    base = workloads.WORKLOADS[args.workload]
+    spec = workloads.tree_spec(base)
+    if spec["rank_hit"] is None:
+        raise SystemExit("--budget needs a workload whose tree grows from a rank-hit table")
+    nodes = [8, 16, 24, 32, 48, 64, 96, 128]
+    contexts = [1024, 4096, 16384]
+    layers = 32
+    ceiling = read_ceiling_gbs(torch, M)
+    fixed_us = args.backbone_gb * 1e9 / (ceiling * 1e9) * 1e6
+    ev = HipEvents()
+    e0, e1 = ev.create(), ev.create()
+    sptr = torch.cuda.current_stream().cuda_stream
+    dt = torch.bfloat16 if base.dtype == "bf16" else torch.float32
+    dcode = M.BF16 if base.dtype == "bf16" else M.F32
+    out = {}
+    for P in contexts:
+        w = dataclasses.replace(base, P=P, n_nodes=max(nodes))
+        x = workloads.draw_round(w, seed=w.seed + 500)
+        S = x["S_max"]
+        per_set = 2 * w.B * w.Hkv * S * w.d * (2 if dt == torch.bfloat16 else 4)
+        n_sets = max(2, -(-512 * 2 ** 20 // per_set))
+        kc = [torch.from_numpy(x["k_cache"]).to("cuda", dt) for _ in range(n_sets)]
+        vc = [torch.from_numpy(x["v_cache"]).to("cuda", dt) for _ in range(n_sets)]
+        times = []
+        for N in nodes:
+            tree = M.medusa_tree_compile(w.num_heads, w.topk, rank_hit=spec["rank_hit"], n_nodes=N)
+            q = torch.from_numpy(np.ascontiguousarray(x["q"][:, :N])).to("cuda", dt)
+            kn = torch.from_numpy(np.ascontiguousarray(x["k_new"][:, :N])).to("cuda", dt)
+            vn = torch.from_numpy(np.ascontiguousarray(x["v_new"][:, :N])).to("cuda", dt)
+            depth = torch.from_numpy(tree["depth"]).to("cuda")
+            mask = torch.from_numpy(tree["tree_mask"].view(np.int64)).to("cuda")
+            o = torch.empty_like(q)
+            ws = torch.zeros(max(M.medusa_tree_attn_workspace_size(dcode, w.B, w.Hq, w.Hkv, w.d, N, S), 16),
+                             dtype=torch.uint8, device="cuda")
+            ctl = torch.from_numpy(np.concatenate([x["prefix_len"], [0]]).astype(np.int32)).to("cuda")
+            lib = M.load()
+            reps, warm = 30, 5
+            ms = []
+            for r in range(warm + reps):
+                k, v = kc[r % n_sets], vc[r % n_sets]
+                rc = lib.medusa_tree_attn(sptr, dcode, w.B, w.Hq, w.Hkv, w.d, N, depth.data_ptr(),
+                                          mask.data_ptr(), tree["mask_words"], ctl.data_ptr(), q.data_ptr(),
+                                          kn.data_ptr(), vn.data_ptr(), k.data_ptr(), v.data_ptr(), S,
+                                          float(w.rope_base), o.data_ptr(), ws.data_ptr(), ws.numel(),
+                                          ctl[w.B:].data_ptr(), e0, e1)
+                if rc:
+                    raise RuntimeError(f"medusa_tree_attn failed ({rc}) at P={P} N={N}")
+                torch.cuda.synchronize()
+                if r >= warm:
+                    ms.append(ev.elapsed_ms(e0, e1))
+            if int(ctl[w.B].item()) != 0:
+                raise RuntimeError(f"device status {int(ctl[w.B].item())} at P={P} N={N}")
+            times.append(float(np.median(ms)) * 1e3)
+            log(f"[bench] budget sweep P={P} N={N}: attention {times[-1]:.2f} us")
+        best, et, rt = M.medusa_tree_budget(spec["rank_hit"], nodes, times, fixed_us, layers)
+        out[str(P)] = {"attention_us": dict(zip(map(str, nodes), times)), "best_n": best,
+                       "expected_tokens": float(et[best]),
+                       "tokens_per_s_per_sequence": float(rt[best]) * 1e6,
+                       "tokens_per_s_at_64": float(rt[64]) * 1e6 if len(rt) > 64 else None}
+        log(f"[bench] budget P={P}: best N={best} ({et[best]:.3f} tokens per round, "
+            f"{rt[best] * 1e6:.1f} tokens/s per sequence; N=64: {rt[64] * 1e6:.1f})")
+        del kc, vc
+        torch.cuda.empty_cache()
+    ev.destroy(e0)
+    ev.destroy(e1)
+    print(json.dumps({"metric": "node budget per context (medusa_tree_budget over measured attention cost)",
+                      "workload": f"{base.name}: B={base.B}, Hq={base.Hq}, Hkv={base.Hkv}, d_h={base.d}, "
+                                  f"greedy trees from the K={base.num_heads}, TOPK={base.topk} rank table",
+                      "layers": layers, "backbone_gb": args.backbone_gb, "read_ceiling_gbs": ceiling,
+                      "fixed_us": fixed_us, "nodes": nodes, "contexts": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +313,11 @@ def main():
                     help="greedy rounds: accept and compact in one call (fused) or two")
     ap.add_argument("--graph", action="store_true",
                     help="also time the same number of steps replayed from one captured HIP graph")
+    ap.add_argument("--budget", action="store_true",
+                    help="sweep the attention call over tree sizes and contexts and choose the node "
+                         "budget per context (medusa_tree_budget); prints its own JSON line")
+    ap.add_argument("--backbone-gb", type=float, default=16.0,
+                    help="--budget: backbone weight bytes streamed once per round (GB)")
     ap.add_argument("--round", choices=["verify", "full"], default="verify",
                     help="full: the Medusa head step fills the candidates first in every step")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for > 512 MB)")
@@ -254,6 +336,9 @@ def main():
     import medusa_tree_attention_amd as M
     import workloads
 
+    if args.budget:
+        budget_sweep(args, np, torch, M, workloads)
+        return
     w = workloads.WORKLOADS[args.workload]
     if args.prefix:
         import dataclasses

@@ -11,6 +11,7 @@
  *   medusa_accept_commit    device: greedy acceptance, compaction and the frontier carry
  *                           in one call
  *   medusa_head_candidates  device: the Medusa heads' top-k candidate rows
+ *   medusa_tree_budget      host:   the node budget with the most tokens per unit time
  *
  * Pages cited (by title and section):
  *   [M7.2]  "M7.2 - Medusa: Multi-Head Candidates, Tree Attention, and Verification"
@@ -127,6 +128,31 @@ typedef struct {
 } medusa_tree;
 
 medusa_status medusa_tree_compile(const medusa_tree_spec* spec, medusa_tree* out);
+
+/* ------------------------------------------------------------------ tree budget (host)
+ *
+ * [M7.2] §0x04C: maximising the expected accepted length per round is not maximising tokens
+ * per second, because nodes carry kernel and cache costs; [Chai] "局限与适用场景": attention
+ * traffic grows with context length and node count, so the best node count changes with the
+ * context length.  For the nested greedy trees T_N of medusa_tree_compile (mode B: T_N is
+ * the first N - 1 admissions of the growth), N rows including the root:
+ *   E[A](N) = sum of T_N's non-root path weights ([M7.2] §0x04B)
+ *   t(N)    = the per-layer cost of the tree-dependent work at the round's context length,
+ *             linear between the measured points (cost_nodes[i], cost_us[i]), cost_nodes
+ *             strictly increasing
+ *   rate(N) = (1 + E[A](N)) / (fixed_us + n_layers * t(N))   (published tokens per us)
+ * *best_n = the N in [cost_nodes[0], cost_nodes[n_costs - 1]] with the largest rate, the
+ * smallest on ties.  Optional host outputs of cost_nodes[n_costs - 1] + 1 doubles, indexed
+ * by N: expected_tokens[N] = 1 + E[A](N), rate[N] (0 outside the measured range).
+ * fixed_us is the tree-independent cost of a round (for example the backbone weight stream).
+ * Errors: MEDUSA_EINVAL (NULL pointer, non-increasing or non-positive node counts, a negative
+ * or non-finite cost, rank_hit outside [0, 1], a round that would cost nothing),
+ * MEDUSA_ECAPACITY (more rows than the rank table can hold).  Host only.
+ */
+medusa_status medusa_tree_budget(const double* rank_hit, int32_t num_heads, int32_t topk, int32_t n_costs,
+                                 const int32_t* cost_nodes, const double* cost_us, double fixed_us,
+                                 int32_t n_layers, int32_t* best_n, double* expected_tokens,
+                                 double* rate);
 
 /* ------------------------------------------------------------------ tree attention
  *

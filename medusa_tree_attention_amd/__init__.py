@@ -14,5 +14,5 @@ from ._binding import (  # noqa: F401
     medusa_accept_typical,
     medusa_accept_workspace_size, medusa_head_candidates, medusa_head_workspace_size,
     medusa_kv_compact, medusa_read_probe, medusa_read_probe_sink_size, medusa_tree_attn,
-    medusa_tree_attn_workspace_size, medusa_tree_compile,
+    medusa_tree_attn_workspace_size, medusa_tree_budget, medusa_tree_compile,
 )

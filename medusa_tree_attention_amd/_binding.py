@@ -64,6 +64,7 @@ _SIGNATURES = {
                                       _SZ, _P, _P, _P]),
     "medusa_kv_compact": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32,
                                  _I32, _P, _P, _P, _P, _P, _P]),
+    "medusa_tree_budget": (_I32, [_P, _I32, _I32, _I32, _P, _P, _D, _I32, _P, _P, _P]),
     "medusa_read_probe_sink_size": (_SZ, []),
     "medusa_read_probe": (_I32, [_P, _P, _SZ, _P, _P, _P]),
     "medusa_accept_commit": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P,
@@ -161,6 +162,25 @@ def medusa_tree_compile(num_heads, topk, paths=None, rank_hit=None, n_nodes=0):
     _check("medusa_tree_compile", lib.medusa_tree_compile(ctypes.byref(spec), ctypes.byref(tree)))
     out.update(n_nodes=n, n_paths=npaths, path_width=w, mask_words=words)
     return out
+
+
+def medusa_tree_budget(rank_hit, cost_nodes, cost_us, fixed_us, n_layers):
+    """Best node count for measured per-layer costs; returns (best_n, expected_tokens, rate),
+    the arrays indexed by the node count."""
+    lib = load()
+    a, pa = _arr(np.asarray(rank_hit, np.float64).reshape(-1), np.float64, ctypes.c_double)
+    K, TOPK = np.asarray(rank_hit).shape
+    nodes, pn = _arr(cost_nodes, np.int32, ctypes.c_int32)
+    us, pu = _arr(cost_us, np.float64, ctypes.c_double)
+    hi = int(nodes[-1])
+    et = np.zeros(hi + 1, np.float64)
+    rt = np.zeros(hi + 1, np.float64)
+    best = ctypes.c_int32(0)
+    code = lib.medusa_tree_budget(pa, K, TOPK, len(nodes), pn, pu, float(fixed_us), int(n_layers),
+                                  ctypes.byref(best), et.ctypes.data_as(ctypes.c_void_p),
+                                  rt.ctypes.data_as(ctypes.c_void_p))
+    _check("medusa_tree_budget", code)
+    return int(best.value), et, rt
 
 
 # ------------------------------------------------------------------ tree attention

@@ -63,7 +63,8 @@ int64_t tuple_count(int32_t K, int32_t topk, int64_t cap) {
   return total;
 }
 
-medusa_status grow_greedy(const medusa_tree_spec& s, std::vector<Path>& paths) {
+medusa_status grow_greedy(const medusa_tree_spec& s, std::vector<Path>& paths,
+                          std::vector<double>* weights = nullptr) {
   const int32_t K = s.num_heads, topk = s.topk;
   for (int64_t i = 0; i < int64_t(K) * topk; ++i) {
     const double a = s.rank_hit[i];
@@ -88,6 +89,7 @@ medusa_status grow_greedy(const medusa_tree_spec& s, std::vector<Path>& paths) {
       }
     }
     paths.push_back(std::move(best.p));
+    if (weights) weights->push_back(best.w);
   }
   return MEDUSA_OK;
 }
@@ -207,5 +209,63 @@ extern "C" medusa_status medusa_tree_compile(const medusa_tree_spec* spec, medus
   out->n_paths = n_leaves;
   out->path_width = width;
   out->mask_words = words;
+  return MEDUSA_OK;
+}
+
+// Context-dependent budget.  [M7.2] §0x04C: the greedy search maximises the expected accepted
+// length per round, which is not tokens per second, since nodes carry kernel costs; [Chai]
+// "局限与适用场景": the attention traffic grows with context length and node count, so the best
+// node count changes with context length.  The tree of budget N is the first N - 1
+// admissions of the greedy growth, so E[A](N) is their weights' running sum (admission
+// order, binary64), and the round rate is (1 + E[A](N)) / (fixed_us + n_layers * t(N)).
+extern "C" medusa_status medusa_tree_budget(const double* rank_hit, int32_t num_heads, int32_t topk,
+                                            int32_t n_costs, const int32_t* cost_nodes,
+                                            const double* cost_us, double fixed_us, int32_t n_layers,
+                                            int32_t* best_n, double* expected_tokens, double* rate) {
+  if (!rank_hit || !cost_nodes || !cost_us || !best_n || num_heads < 1 || topk < 1 || n_costs < 1 ||
+      n_layers < 0 || !(fixed_us >= 0.0) || !std::isfinite(fixed_us))
+    return MEDUSA_EINVAL;
+  for (int32_t i = 0; i < n_costs; ++i) {
+    if (cost_nodes[i] < 1 || (i > 0 && cost_nodes[i] <= cost_nodes[i - 1])) return MEDUSA_EINVAL;
+    if (!(cost_us[i] >= 0.0) || !std::isfinite(cost_us[i])) return MEDUSA_EINVAL;
+  }
+  const int32_t lo = cost_nodes[0], hi = cost_nodes[n_costs - 1];
+  medusa_tree_spec s{};
+  s.num_heads = num_heads;
+  s.topk = topk;
+  s.rank_hit = rank_hit;
+  s.n_nodes = hi;
+  std::vector<Path> paths;
+  std::vector<double> w;
+  const medusa_status st = grow_greedy(s, paths, &w);
+  if (st != MEDUSA_OK) return st;
+  if (fixed_us == 0.0 && n_layers == 0) return MEDUSA_EINVAL;  // a round would cost nothing
+  int32_t seg = 0;
+  double ea = 0.0, best_rate = -1.0;
+  int32_t best = lo;
+  for (int32_t n = 1; n <= hi; ++n) {
+    if (n >= 2) ea += w[size_t(n) - 2];
+    if (n < lo) {
+      if (expected_tokens) expected_tokens[n] = 1.0 + ea;
+      if (rate) rate[n] = 0.0;
+      continue;
+    }
+    while (seg + 1 < n_costs - 1 && cost_nodes[seg + 1] < n) ++seg;
+    double t = cost_us[seg];
+    if (n_costs > 1) {
+      const int32_t n0 = cost_nodes[seg], n1 = cost_nodes[seg + 1];
+      t = cost_us[seg] + (cost_us[seg + 1] - cost_us[seg]) * double(n - n0) / double(n1 - n0);
+    }
+    const double r = (1.0 + ea) / (fixed_us + double(n_layers) * t);
+    if (expected_tokens) expected_tokens[n] = 1.0 + ea;
+    if (rate) rate[n] = r;
+    if (r > best_rate) {
+      best_rate = r;
+      best = n;
+    }
+  }
+  if (expected_tokens) expected_tokens[0] = 0.0;
+  if (rate) rate[0] = 0.0;
+  *best_n = best;
   return MEDUSA_OK;
 }
