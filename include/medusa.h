@@ -324,7 +324,8 @@ medusa_status medusa_accept_commit(void* stream, int32_t B, int32_t N, int32_t V
  * Arithmetic in fp32 (inputs widened, products accumulated in fp32).  Weights are read once
  * per group of four sequences.
  * Workspace: at least medusa_head_workspace_size(B, K, d, V) bytes of device memory; it
- * receives u = SiLU(W1 h) + h and, without head_logits, the logits.
+ * receives u = SiLU(W1 h) + h and the ranked lists of the unembedding row blocks (the
+ * logits are ranked where they are computed and written to memory only into head_logits).
  * Host errors: MEDUSA_EINVAL (non-positive size, NULL pointer, h, W1 or W2 not 16-byte
  * aligned), MEDUSA_EUNSUPPORTED (d not a multiple of 8 or above 8192, topk above 64 or above
  * V, one head's W2 or the fp32 inputs of one head 4 GiB or larger), MEDUSA_EBUFSIZE.

@@ -29,13 +29,16 @@
 //    columns and add their sums through LDS.
 //  * The residual kernel writes u = SiLU(W1 h) + h in fp32; the unembedding kernel writes
 //    the logits in fp32.
-//  * Top-k in two passes: one 256-thread workgroup per 2048-logit segment of a (head,
-//    sequence) row ranks its segment's best topk, then one workgroup per row merges the
-//    segments' lists.  An entry is ranked by one 64-bit key (value order in the high word,
-//    inverted index in the low word, so among equal logits the lower token id ranks
-//    first); round r takes the largest key below round r-1's winner by a workgroup
-//    maximum (DPP within a wavefront, LDS across wavefronts, one barrier per round).
+//  * Top-k in two passes: every unembedding workgroup ranks the best topk of its (at most
+//    512) rows per column right after computing them -- the logits go to LDS, one wavefront
+//    per column takes rounds over ranking keys held in registers, without barriers -- and
+//    one workgroup per (head, sequence) then merges the workgroups' lists.  An entry is
+//    ranked by one 64-bit key (value order in the high word, inverted index in the low
+//    word, so among equal logits the lower token id ranks first); round r takes the
+//    largest key below round r-1's winner (DPP maxima within a wavefront).  The logits
+//    themselves are written only when the caller asks for them.
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -47,11 +50,9 @@ namespace {
 constexpr int kGemvThreads = 512;
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kGemvRows = 8;      // rows per wavefront group
+constexpr int kBlockRows = 512;   // output rows per workgroup at most (staged in LDS; ranked in registers)
 constexpr int kCols = 4;          // input columns per launch
 constexpr int kPad = 512;         // LDS columns are zero-padded to a multiple of this
-constexpr int kSegThreads = 256;
-constexpr int kSegPerThread = 8;
-constexpr int kSegLen = kSegThreads * kSegPerThread;  // logits per top-k segment
 constexpr int kMergeThreads = 256;
 constexpr int kMergeCache = 8;    // list keys per merge thread held in registers
 constexpr int kMaxTopk = 64;
@@ -60,21 +61,71 @@ constexpr int kTargetWaves = 256 * 16;  // 16 wavefronts on each of 256 compute 
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// The ranking as one unsigned 64-bit key: the high word maps the float order onto the
+// unsigned order (negative values bit-inverted, non-negative ones with the sign bit set;
+// -0 is taken as +0 first), the low word is the inverted index, so the largest key is the
+// largest value and, among equal values, the lowest index.  Key 0 lies below every real
+// entry (it stands for "none"); a NaN never gets a key (it is reported instead).
+__device__ __forceinline__ uint64_t rank_key(float v, int i) {
+  unsigned b = __float_as_uint(v == 0.f ? 0.f : v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (uint64_t(b) << 32) | uint64_t(~unsigned(i));
+}
+__device__ __forceinline__ int key_index(uint64_t key) { return int(~unsigned(key)); }
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const unsigned lo = __builtin_amdgcn_update_dpp(0u, unsigned(x), kCtrl, 0xf, 0xf, false);
+  const unsigned hi = __builtin_amdgcn_update_dpp(0u, unsigned(x >> 32), kCtrl, 0xf, 0xf, false);
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int lane) {
+  const unsigned lo = __builtin_amdgcn_readlane(unsigned(x), lane);
+  const unsigned hi = __builtin_amdgcn_readlane(unsigned(x >> 32), lane);
+  return (uint64_t(hi) << 32) | lo;
+}
+// maximum over the wavefront (all lanes active), uniform: the quad swaps, the half-row and
+// row mirrors leave every row of 16 lanes with its maximum, then the four rows are read out
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t x) {
+  x = max_u64(x, dpp_u64<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = max_u64(x, dpp_u64<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = max_u64(x, dpp_u64<0x141>(x));  // row_half_mirror
+  x = max_u64(x, dpp_u64<0x140>(x));  // row_mirror
+  return max_u64(max_u64(readlane_u64(x, 0), readlane_u64(x, 16)),
+                 max_u64(readlane_u64(x, 32), readlane_u64(x, 48)));
+}
+// maximum over the workgroup; slot[2][waves] alternates by round so that one barrier per
+// round suffices (a slot is rewritten two rounds later, after the next barrier)
+template <int kThreads>
+__device__ __forceinline__ uint64_t block_max_key(uint64_t x, uint64_t (*slot)[kThreads / 64], int round) {
+  const int wave = threadIdx.x >> 6;
+  x = wave_max_key(x);
+  if ((threadIdx.x & 63) == 0) slot[round & 1][wave] = x;
+  __syncthreads();
+  x = slot[round & 1][0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) x = max_u64(x, slot[round & 1][w]);
+  return x;
+}
+
+constexpr uint64_t kNanList = ~uint64_t(0);  // marks a ranked list whose rows hold a NaN
+
 struct GemvArgs {
   const bf16* W;        // [K][R][d]
   const bf16* x_bf16;   // residual kernel: h [B][d]
   const float* x_f32;   // unembedding kernel: u [K][B][d]
-  float* out;           // [K][B][R]
-  const int32_t* status;
-  int32_t B, d, dpad, R, col0, ncols, rows_per_block, split;
+  float* out;           // [K][B][R]; the unembedding kernel's logits, or null
+  int32_t* status;
+  uint64_t* keys;       // unembedding kernel: [K][B][nblk][topk] ranked keys per row block
+  int32_t B, d, dpad, R, col0, ncols, rows_per_block, split, topk, nblk;
 };
 
 struct TopkArgs {
-  const float* logits;  // [K][B][V]
   const int32_t* root;  // [B]
   int32_t* candidates;  // [B][1 + K topk]
   int32_t* status;
-  uint64_t* seg_keys;   // [K][B][S][topk] ranking keys
+  uint64_t* seg_keys;   // [K][B][S][topk] ranked keys of the unembedding row blocks
   int32_t B, K, V, topk, S;
 };
 
@@ -84,7 +135,6 @@ __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w 
 template <bool kResidual>
 __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void head_gemv_kernel(GemvArgs g) {
-  const bool failed = round_failed(g.status);  // gates the stores only
   __shared__ float part[kGemvWaves][32];       // split row groups: partial sums
   extern __shared__ float xs[];                // [kCols][dpad], zero past d
   const int k = blockIdx.y;
@@ -214,16 +264,19 @@ void head_gemv_kernel(GemvArgs g) {
     }
     return v[0] + __shfl_xor(v[0], 1, 64);
   };
+  // this block's outputs [kCols][rows], written out at the end (so that the status word is
+  // needed only there)
+  float* blk = xs + kCols * g.dpad;
   auto store = [&](int base, float total) __attribute__((always_inline)) {
     const int idx = lane >> 1, r = idx >> 2, c = idx & 3;
     const int row = base + r;
-    if (!failed && (lane & 1) == 0 && row < r1 && c < g.ncols) {
+    if ((lane & 1) == 0 && row < r1 && c < g.ncols) {
       float v = total;
       if (kResidual) {
         const float x = xs[c * g.dpad + row];  // the residual input h (R = d)
         v = v / (1.0f + expf(-v)) + x;         // SiLU(W1 h) + h
       }
-      g.out[(int64_t(k) * g.B + g.col0 + c) * g.R + row] = v;
+      blk[c * g.rows_per_block + (row - r0)] = v;
     }
   };
 
@@ -293,97 +346,52 @@ void head_gemv_kernel(GemvArgs g) {
       store(first, total);
     }
   }
-}
-
-// The ranking as one unsigned 64-bit key: the high word maps the float order onto the
-// unsigned order (negative values bit-inverted, non-negative ones with the sign bit set;
-// -0 is taken as +0 first), the low word is the inverted index, so the largest key is the
-// largest value and, among equal values, the lowest index.  Key 0 lies below every real
-// entry (it stands for "none"); a NaN never gets a key (it is reported instead).
-__device__ __forceinline__ uint64_t rank_key(float v, int i) {
-  unsigned b = __float_as_uint(v == 0.f ? 0.f : v);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return (uint64_t(b) << 32) | uint64_t(~unsigned(i));
-}
-__device__ __forceinline__ int key_index(uint64_t key) { return int(~unsigned(key)); }
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-template <int kCtrl>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
-  const unsigned lo = __builtin_amdgcn_update_dpp(0u, unsigned(x), kCtrl, 0xf, 0xf, false);
-  const unsigned hi = __builtin_amdgcn_update_dpp(0u, unsigned(x >> 32), kCtrl, 0xf, 0xf, false);
-  return (uint64_t(hi) << 32) | lo;
-}
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int lane) {
-  const unsigned lo = __builtin_amdgcn_readlane(unsigned(x), lane);
-  const unsigned hi = __builtin_amdgcn_readlane(unsigned(x >> 32), lane);
-  return (uint64_t(hi) << 32) | lo;
-}
-// maximum over the wavefront (all lanes active), uniform: the quad swaps, the half-row and
-// row mirrors leave every row of 16 lanes with its maximum, then the four rows are read out
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t x) {
-  x = max_u64(x, dpp_u64<0xB1>(x));   // quad_perm [1, 0, 3, 2]
-  x = max_u64(x, dpp_u64<0x4E>(x));   // quad_perm [2, 3, 0, 1]
-  x = max_u64(x, dpp_u64<0x141>(x));  // row_half_mirror
-  x = max_u64(x, dpp_u64<0x140>(x));  // row_mirror
-  return max_u64(max_u64(readlane_u64(x, 0), readlane_u64(x, 16)),
-                 max_u64(readlane_u64(x, 32), readlane_u64(x, 48)));
-}
-// maximum over the workgroup; slot[2][waves] alternates by round so that one barrier per
-// round suffices (a slot is rewritten two rounds later, after the next barrier)
-template <int kThreads>
-__device__ __forceinline__ uint64_t block_max_key(uint64_t x, uint64_t (*slot)[kThreads / 64], int round) {
-  const int wave = threadIdx.x >> 6;
-  x = wave_max_key(x);
-  if ((threadIdx.x & 63) == 0) slot[round & 1][wave] = x;
-  __syncthreads();
-  x = slot[round & 1][0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) x = max_u64(x, slot[round & 1][w]);
-  return x;
-}
-
-constexpr uint64_t kNanList = ~uint64_t(0);  // marks the list of a segment holding a NaN
-
-// pass 1: the best topk keys of one 2048-logit segment of a (head, sequence) row, best
-// first; a segment with fewer entries ends its list with key 0.  A NaN logit raises
-// MEDUSA_EINVAL and marks the list.
-__global__ __launch_bounds__(kSegThreads) void head_topk_segment_kernel(TopkArgs a) {
-  __shared__ uint64_t slot[2][kSegThreads / 64];
-  const int s = blockIdx.x % a.S, kb = blockIdx.x / a.S;  // kb = head * B + sequence
-  const int tid = threadIdx.x;
-  const int lo = s * kSegLen, n = min(kSegLen, a.V - lo);
-  const float* row = a.logits + int64_t(kb) * a.V + lo;
-  uint64_t* out = a.seg_keys + (int64_t(kb) * a.S + s) * a.topk;
-  float z[kSegPerThread];
-#pragma unroll
-  for (int q = 0; q < kSegPerThread; ++q) z[q] = row[min(tid + q * kSegThreads, n - 1)];  // all loads first
-  uint64_t key[kSegPerThread];
-  bool nan = false;
-#pragma unroll
-  for (int q = 0; q < kSegPerThread; ++q) {
-    const int i = tid + q * kSegThreads;
-    nan = nan || (z[q] != z[q]);
-    key[q] = i < n ? rank_key(z[q], lo + i) : 0;
+  __syncthreads();  // every output of the block is in blk
+  const bool failed = round_failed(g.status);  // gates the output stores only
+  if (!failed && g.out) {  // coalesced: consecutive threads write consecutive rows
+    const int n = r1 - r0;
+    for (int i = tid; i < g.ncols * g.rows_per_block; i += kGemvThreads) {
+      const int c = i / g.rows_per_block, r = i - c * g.rows_per_block;
+      if (r < n) g.out[(int64_t(k) * g.B + g.col0 + c) * g.R + r0 + r] = blk[i];
+    }
   }
-  if (__syncthreads_or(nan)) {
-    if (tid == 0) raise_status(a.status, MEDUSA_EINVAL);
-    if (tid < a.topk) out[tid] = kNanList;
-    return;
-  }
-  uint64_t prev = ~uint64_t(0);  // keys below prev remain
-  for (int r = 0; r < a.topk; ++r) {
-    uint64_t best = 0;
+  if (!kResidual) {
+    // The block's best topk rows of every column, best first, as ranking keys (key 0 past
+    // the block's rows): one wavefront per column, the keys in registers (at most
+    // kBlockRows / 64 per lane), rounds without barriers.
+    if (wave < g.ncols) {
+      const int c = wave, n = r1 - r0;
+      uint64_t key[kBlockRows / 64];
+      bool nan = false;
 #pragma unroll
-    for (int q = 0; q < kSegPerThread; ++q)
-      if (key[q] < prev) best = max_u64(best, key[q]);
-    best = block_max_key<kSegThreads>(best, slot, r);
-    if (tid == 0) out[r] = best;
-    prev = best;
+      for (int q = 0; q < kBlockRows / 64; ++q) {
+        const int i = lane + 64 * q;
+        const float v = blk[c * g.rows_per_block + (i < n ? i : 0)];
+        nan = nan || (i < n && v != v);
+        key[q] = i < n && v == v ? rank_key(v, r0 + i) : 0;
+      }
+      uint64_t* out = g.keys + ((int64_t(k) * g.B + g.col0 + c) * g.nblk + blockIdx.x) * g.topk;
+      if (__ballot(nan)) {
+        if (lane == 0) raise_status(g.status, MEDUSA_EINVAL);
+        for (int r = lane; r < g.topk; r += 64) out[r] = kNanList;
+      } else {
+        uint64_t prev = ~uint64_t(0);  // keys below prev remain
+        for (int r = 0; r < g.topk; ++r) {
+          uint64_t best = 0;
+#pragma unroll
+          for (int q = 0; q < kBlockRows / 64; ++q)
+            if (key[q] < prev) best = max_u64(best, key[q]);
+          best = wave_max_key(best);
+          if (lane == 0) out[r] = best;
+          prev = best;
+        }
+      }
+    }
   }
 }
 
-// pass 2: one workgroup per (head, sequence) merges the segments' lists into candidate
+
+// One workgroup per (head, sequence) merges the row blocks' lists into candidate
 // slots 1 + head topk + r, and head 0's workgroups write the root token into slot 0.  Up to
 // kMergeCache keys per thread are held in registers; longer lists are re-read each round.
 template <bool kCached>
@@ -432,21 +440,58 @@ __global__ __launch_bounds__(kMergeThreads) void head_topk_merge_kernel(TopkArgs
   if (tid == 0 && k == 0 && !failed) cand[0] = a.root[b];
 }
 
+// Launch shape of one GEMV over R rows: row groups of 8; with fewer groups than wavefronts
+// to fill the chip, 2..8 wavefronts share a group (each taking every split-th column of
+// pieces), one group per wavefront; otherwise about per_cu workgroups per compute unit and
+// head, each over a contiguous row range (at most max_rows rows, a multiple of 64).
+struct GemvShape {
+  int32_t split, rows_per_block, blocks;
+};
+
+GemvShape gemv_shape(int32_t R, int32_t K, int32_t dpad, int32_t per_cu, int32_t max_rows) {
+  GemvShape sh{};
+  const int64_t groups = int64_t(K) * ((R + kGemvRows - 1) / kGemvRows);
+  const int32_t nch = dpad / kPad;
+  sh.split = 1;
+  while (sh.split < kGemvWaves && sh.split * 2 <= nch && groups * sh.split < kTargetWaves) sh.split *= 2;
+  if (sh.split > 1) {
+    sh.rows_per_block = (kGemvWaves / sh.split) * kGemvRows;
+  } else {
+    const int64_t blocks = (int64_t(256) * per_cu + K - 1) / K;  // per head
+    const int64_t rows = (R + blocks - 1) / blocks;
+    const int64_t unit = int64_t(kGemvWaves) * kGemvRows;
+    sh.rows_per_block = int32_t(std::min<int64_t>((rows + unit - 1) / unit * unit, max_rows));
+  }
+  sh.blocks = (R + sh.rows_per_block - 1) / sh.rows_per_block;
+  return sh;
+}
+
+int32_t dpad_of(int32_t d) { return (d + kPad - 1) / kPad * kPad; }
+
+// dynamic LDS of the two GEMV kernels: the input columns and the block's staged outputs
+size_t lds_residual(int32_t dpad) { return size_t(kCols) * (dpad + kBlockRows) * sizeof(float); }
+size_t lds_unembed(int32_t dpad) { return size_t(kCols) * (dpad + kBlockRows) * sizeof(float); }
+int32_t resident(size_t lds) { return (160 * 1024) / (lds + 1024) >= 2 ? 2 : 1; }
+
+GemvShape unembed_shape(int32_t K, int32_t d, int32_t V) {
+  const int32_t dpad = dpad_of(d);
+  return gemv_shape(V, K, dpad, resident(lds_unembed(dpad)), kBlockRows);
+}
+
 struct HeadPlan {
-  size_t u_offset, logits_offset, keys_offset, bytes;
-  int32_t segments;
+  size_t u_offset, keys_offset, bytes;
+  int32_t nblk;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// segment lists are sized for the largest topk, so the size depends on the shapes only
+// the ranked lists are sized for the largest topk, so the size depends on the shapes only
 HeadPlan head_plan(int32_t B, int32_t K, int32_t d, int32_t V) {
   HeadPlan p{};
-  p.segments = (V + kSegLen - 1) / kSegLen;
-  const size_t lists = size_t(K) * B * p.segments * kMaxTopk;
+  p.nblk = unembed_shape(K, d, V).blocks;
+  const size_t lists = size_t(K) * B * p.nblk * kMaxTopk;
   p.u_offset = 0;
-  p.logits_offset = align256(size_t(K) * B * d * sizeof(float));
-  p.keys_offset = p.logits_offset + align256(size_t(K) * B * V * sizeof(float));
+  p.keys_offset = align256(size_t(K) * B * d * sizeof(float));
   p.bytes = p.keys_offset + align256(lists * sizeof(uint64_t));
   return p;
 }
@@ -479,74 +524,63 @@ extern "C" medusa_status medusa_head_candidates(void* stream, int32_t B, int32_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* u = reinterpret_cast<float*>(ws + plan.u_offset);
-  float* logits = head_logits ? head_logits : reinterpret_cast<float*>(ws + plan.logits_offset);
-  const int32_t dpad = (d + kPad - 1) / kPad * kPad;
-  const size_t lds = size_t(kCols) * dpad * sizeof(float);  // plus 1 KiB of static partials
-  if (lds > 60 * 1024) {  // beyond the default dynamic LDS of a launch
-    for (const void* kern : {reinterpret_cast<const void*>(&head_gemv_kernel<true>),
-                             reinterpret_cast<const void*>(&head_gemv_kernel<false>)})
-      if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
-        return MEDUSA_EHIP;
-  }
-  // workgroups resident per compute unit (160 KiB of LDS each) and the launch shape
-  const int32_t per_cu = int32_t((160 * 1024) / (lds + 1024)) >= 2 ? 2 : 1;
-  auto gemv = [&](bool residual, const void* W, int32_t R, float* out, int32_t col0, void* e0) -> medusa_status {
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ws + plan.keys_offset);
+  const int32_t dpad = dpad_of(d);
+  const size_t lds_r = lds_residual(dpad), lds_u = lds_unembed(dpad);
+  // beyond the default dynamic LDS of a launch
+  if (lds_r > 60 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&head_gemv_kernel<true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_r)) != hipSuccess)
+    return MEDUSA_EHIP;
+  if (lds_u > 60 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&head_gemv_kernel<false>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_u)) != hipSuccess)
+    return MEDUSA_EHIP;
+  const GemvShape sh_r = gemv_shape(d, K, dpad, resident(lds_r), kBlockRows);
+  const GemvShape sh_u = unembed_shape(K, d, V);
+  auto gemv = [&](bool residual, int32_t col0, void* e0, void* e1) -> medusa_status {
+    const GemvShape& sh = residual ? sh_r : sh_u;
     GemvArgs g{};
-    g.W = static_cast<const bf16*>(W);
+    g.W = static_cast<const bf16*>(residual ? W1 : W2);
     g.x_bf16 = static_cast<const bf16*>(h);
     g.x_f32 = u;
-    g.out = out;
+    g.out = residual ? u : head_logits;
     g.status = d_status;
+    g.keys = keys;
     g.B = B;
     g.d = d;
     g.dpad = dpad;
-    g.R = R;
+    g.R = residual ? d : V;
     g.col0 = col0;
     g.ncols = B - col0 < kCols ? B - col0 : kCols;
-    // row groups of 8; with fewer groups than wavefronts to fill the chip, 2..8 wavefronts
-    // share a group (each taking every split-th column of pieces), one group per wavefront
-    const int64_t groups = int64_t(K) * ((R + kGemvRows - 1) / kGemvRows);
-    const int32_t nch = dpad / kPad;
-    int32_t split = 1;
-    while (split < kGemvWaves && split * 2 <= nch && groups * split < kTargetWaves) split *= 2;
-    g.split = split;
-    if (split > 1) {
-      g.rows_per_block = (kGemvWaves / split) * kGemvRows;
-    } else {
-      const int64_t blocks = (int64_t(256) * per_cu + K - 1) / K;  // per head
-      const int64_t rows = (R + blocks - 1) / blocks;
-      const int64_t unit = int64_t(kGemvWaves) * kGemvRows;
-      g.rows_per_block = int32_t((rows + unit - 1) / unit * unit);
-    }
-    const dim3 grid(unsigned((R + g.rows_per_block - 1) / g.rows_per_block), unsigned(K));
+    g.rows_per_block = sh.rows_per_block;
+    g.split = sh.split;
+    g.topk = topk;
+    g.nblk = sh.blocks;
     const void* kern = residual ? reinterpret_cast<const void*>(&head_gemv_kernel<true>)
                                 : reinterpret_cast<const void*>(&head_gemv_kernel<false>);
-    return launch(kern, grid, dim3(kGemvThreads), lds, s, g, e0, nullptr);
+    return launch(kern, dim3(unsigned(sh.blocks), unsigned(K)), dim3(kGemvThreads), residual ? lds_r : lds_u, s,
+                  g, e0, e1);
   };
   for (int32_t c0 = 0; c0 < B; c0 += kCols) {
-    medusa_status st = gemv(true, W1, d, u, c0, c0 == 0 ? ev_start : nullptr);
+    medusa_status st = gemv(true, c0, c0 == 0 ? ev_start : nullptr, nullptr);
     if (st != MEDUSA_OK) return st;
   }
   for (int32_t c0 = 0; c0 < B; c0 += kCols) {
-    medusa_status st = gemv(false, W2, V, logits, c0, nullptr);
+    medusa_status st = gemv(false, c0, nullptr, nullptr);
     if (st != MEDUSA_OK) return st;
   }
   TopkArgs t{};
-  t.logits = logits;
   t.root = d_root_tokens;
   t.candidates = candidates;
   t.status = d_status;
-  t.seg_keys = reinterpret_cast<uint64_t*>(ws + plan.keys_offset);
+  t.seg_keys = keys;
   t.B = B;
   t.K = K;
   t.V = V;
   t.topk = topk;
-  t.S = plan.segments;
-  medusa_status st = launch(reinterpret_cast<const void*>(&head_topk_segment_kernel),
-                            dim3(unsigned(int64_t(K) * B * plan.segments)), dim3(kSegThreads), 0, s, t,
-                            nullptr, nullptr);
-  if (st != MEDUSA_OK) return st;
-  const void* merge = int64_t(plan.segments) * topk <= int64_t(kMergeThreads) * kMergeCache
+  t.S = plan.nblk;
+  const void* merge = int64_t(plan.nblk) * topk <= int64_t(kMergeThreads) * kMergeCache
                           ? reinterpret_cast<const void*>(&head_topk_merge_kernel<true>)
                           : reinterpret_cast<const void*>(&head_topk_merge_kernel<false>);
   return launch(merge, dim3(unsigned(int64_t(K) * B)), dim3(kMergeThreads), 0, s, t, nullptr, ev_stop);
