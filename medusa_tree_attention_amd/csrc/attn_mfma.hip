@@ -729,6 +729,12 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     // first score MFMA of a tile starts from the accumulator value -m_run, so exp2 takes
     // the accumulator directly.  The running maximum is checked at the end of each step,
     // on the scores just formed, and moved (rarely) before they are used.
+    //
+    // The loop runs the per-tile chain scores -> maximum -> probabilities -> P V one tile
+    // apart: step j first issues the P V products of tile j-1, whose operands are already
+    // in registers, so the matrix core has work as soon as the barrier releases while the
+    // probabilities of tile j are formed on the VALU and the K operands of tile j+1 come
+    // from LDS; then it reads the V operands of tile j and forms the scores of tile j+1.
     update_max(s_cur);
     f32x16 negm;
 #pragma unroll
@@ -736,12 +742,29 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       s_cur[e] -= m_run;
       negm[e] = -m_run;
     }
+    // the P V of "tile -1" adds zeros
+    bf16x8 pop[2], vop[2][2][2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pop[t2][e] = static_cast<bf16>(0.0f);
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) vop[dh][j][t2] = pop[0];
     // global addresses of the tiles of stage S-1 (issued by step 0); lane offsets in poff[]
     const bf16* kq = kc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
     const bf16* vq = vc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
     const uint32_t ring0 = lds_addr(&s_ring[0][0]) + 256 * kDmaRows * wave;
-    auto steady = [&](int j, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteadyWait) : "memory");
+    // step j: s holds the relative scores of tile j, pop the probabilities and vop the V
+    // operands of tile j-1; on return s holds the scores of tile j+1, pop and vop those of
+    // tile j
+    auto steady = [&](int j, f32x16& s) __attribute__((always_inline)) {
+      // this wavefront's tile loads of stage j+1 have landed, and its V reads of stage j-1
+      // (issued late in the last step) are done before any wavefront refills that slot
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kSteadyWait) : "memory");
       __syncthreads();  // stage j+1 visible; every wavefront is done with stage j-1
       const uint32_t dst = ring0 + uint32_t(((j + S - 1) & (S - 1)) * n_kp * kTileBytes);
 #pragma unroll
@@ -755,35 +778,41 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       vq += n_kp * kTile * kD;
       const unsigned char* tn = s_ring[((j + 1) & (S - 1)) * n_kp + kp];
       const unsigned char* tc = s_ring[(j & (S - 1)) * n_kp + kp];
-      // every operand read of the step is issued up front
-      bf16x8 kop[2][4], vop[2][2][2];
+      bf16x8 kop[2][4];
       read_k(tn, 0, kop[0]);
       read_k(tn, 1, kop[1]);
+      // P V of tile j-1 while the probabilities of tile j are formed
+      pv(0, vop[0], pop);
+      pv(1, vop[1], pop);
+      probs(s, 0.f, pop);
       read_v(tc, 0, vop[0]);
       read_v(tc, 1, vop[1]);
-      // probabilities of tile j against the running maximum
-      bf16x8 pop[2];
-      probs(sc, 0.f, pop);
       // scores of tile j+1, relative to the running maximum
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kh][jj], qop[4 * kh + jj], kh == 0 && jj == 0 ? negm : sn, 0, 0, 0);
-      pv(0, vop[0], pop);
-      pv(1, vop[1], pop);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kh][jj], qop[4 * kh + jj], kh == 0 && jj == 0 ? negm : s, 0, 0, 0);
       // maximum of tile j+1; the reference moves when it exceeds the slack
-      float x0 = max3f(sn[0], sn[1], sn[2]), x1 = max3f(sn[3], sn[4], sn[5]);
-      float x2 = max3f(sn[6], sn[7], sn[8]), x3 = max3f(sn[9], sn[10], sn[11]);
-      float x4 = max3f(sn[12], sn[13], sn[14]);
+      float x0 = max3f(s[0], s[1], s[2]), x1 = max3f(s[3], s[4], s[5]);
+      float x2 = max3f(s[6], s[7], s[8]), x3 = max3f(s[9], s[10], s[11]);
+      float x4 = max3f(s[12], s[13], s[14]);
       x0 = max3f(x0, x1, x2);
-      x3 = max3f(x3, x4, sn[15]);
+      x3 = max3f(x3, x4, s[15]);
       x0 = max2f(x0, x3);
       float y0, y1;
       halves(x0, y0, y1);
       const float tmax = max2f(y0, y1);
       const bool grow = tmax > kRescaleSlack;
       if (__ballot(grow)) {
+        // tile j's P V is still pending against the old reference: add it now, rescale,
+        // and leave zeros for the next step to add
+        pv(0, vop[0], pop);
+        pv(1, vop[1], pop);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pop[t2][e] = static_cast<bf16>(0.0f);
         const float shift = grow ? tmax : 0.f;
         const float corr = exp2_fast(-shift);
         l_run *= corr;
@@ -794,21 +823,15 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
         m_run += shift;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          sn[e] -= shift;
+          s[e] -= shift;
           negm[e] = -m_run;
         }
       }
     };
-    // unrolled twice so that the two score tiles trade places without copies
-    for (; i + 2 <= hot_end; i += 2) {
-      steady(i, s_cur, s_nxt);
-      steady(i + 1, s_nxt, s_cur);
-    }
-    if (i < hot_end) {
-      steady(i, s_cur, s_nxt);
-      s_cur = s_nxt;
-      ++i;
-    }
+    for (; i < hot_end; ++i) steady(i, s_cur);
+    // the last pending P V
+    pv(0, vop[0], pop);
+    pv(1, vop[1], pop);
     // back to absolute scores for the general steps
 #pragma unroll
     for (int e = 0; e < 16; ++e) s_cur[e] += m_run;

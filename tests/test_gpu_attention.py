@@ -129,3 +129,33 @@ def test_repeated_calls_reuse_the_workspace():
     run.kc.copy_(torch.from_numpy(x["k_cache"]).to("cuda", torch.bfloat16))
     assert run.run() == 0
     assert torch.equal(first, run.out)
+
+
+def test_running_maximum_moves_inside_the_key_stream():
+    """Committed keys whose scale climbs from 1 to 6 along each quarter of the context (a
+    sawtooth): the largest score of a key range grows by far more than the 2^8 slack (about
+    3 to 26 in log2 units), so the running maximum moves, with O and l rescaled, in the
+    middle of every workgroup's key stream.  A tile mishandled around a move is off by a
+    factor of at least 2^8 and shows as an error of order |v|.
+
+    Precision: the rotated queries are rounded to bf16 (relative 2^-9) for the matrix
+    core, so a score near 20 carries an absolute error near 0.04, and a peaked softmax
+    passes that on to the output instead of averaging it out.  The values are drawn at a
+    quarter of the unit scale, which keeps that effect (about 5e-3 here) inside the bf16
+    tolerance."""
+    w = dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=8, Hkv=2)
+    announce("attention with a climbing score scale (running-maximum moves)")
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w, seed=31, prefix_len=[4096, 3001])
+    scale = 1.0 + 5.0 * (np.arange(x["S_max"]) % 1024) / 1024
+    x["k_cache"] = workloads.round_to_dtype(
+        x["k_cache"] * scale[None, None, :, None].astype(np.float32), w.dtype)
+    x["v_cache"] = workloads.round_to_dtype(x["v_cache"] * np.float32(0.25), w.dtype)
+    x["v_new"] = workloads.round_to_dtype(x["v_new"] * np.float32(0.25), w.dtype)
+    run = AttnRun(w, x, lib, ora)
+    assert run.run() == 0
+    N = x["N"]
+    must = [(b, u, h) for b in range(w.B) for u in (0, N - 1) for h in (0, w.Hq - 1)]
+    err, staged = run.check(sample_rows(w, N, 96, seed=2, must=must))
+    announce(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.dtype] and staged <= 1.0
