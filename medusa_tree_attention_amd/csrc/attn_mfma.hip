@@ -729,12 +729,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     // first score MFMA of a tile starts from the accumulator value -m_run, so exp2 takes
     // the accumulator directly.  The running maximum is checked at the end of each step,
     // on the scores just formed, and moved (rarely) before they are used.
-    //
-    // The loop runs the per-tile chain scores -> maximum -> probabilities -> P V one tile
-    // apart: step j first issues the P V products of tile j-1, whose operands are already
-    // in registers, so the matrix core has work as soon as the barrier releases while the
-    // probabilities of tile j are formed on the VALU and the K operands of tile j+1 come
-    // from LDS; then it reads the V operands of tile j and forms the scores of tile j+1.
     update_max(s_cur);
     f32x16 negm;
 #pragma unroll
@@ -742,29 +736,12 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       s_cur[e] -= m_run;
       negm[e] = -m_run;
     }
-    // the P V of "tile -1" adds zeros
-    bf16x8 pop[2], vop[2][2][2];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pop[t2][e] = static_cast<bf16>(0.0f);
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) vop[dh][j][t2] = pop[0];
     // global addresses of the tiles of stage S-1 (issued by step 0); lane offsets in poff[]
     const bf16* kq = kc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
     const bf16* vq = vc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
     const uint32_t ring0 = lds_addr(&s_ring[0][0]) + 256 * kDmaRows * wave;
-    // step j: s holds the relative scores of tile j, pop the probabilities and vop the V
-    // operands of tile j-1; on return s holds the scores of tile j+1, pop and vop those of
-    // tile j
-    auto steady = [&](int j, f32x16& s) __attribute__((always_inline)) {
-      // this wavefront's tile loads of stage j+1 have landed, and its V reads of stage j-1
-      // (issued late in the last step) are done before any wavefront refills that slot
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kSteadyWait) : "memory");
+    auto steady = [&](int j, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteadyWait) : "memory");
       __syncthreads();  // stage j+1 visible; every wavefront is done with stage j-1
       const uint32_t dst = ring0 + uint32_t(((j + S - 1) & (S - 1)) * n_kp * kTileBytes);
 #pragma unroll
@@ -778,41 +755,35 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       vq += n_kp * kTile * kD;
       const unsigned char* tn = s_ring[((j + 1) & (S - 1)) * n_kp + kp];
       const unsigned char* tc = s_ring[(j & (S - 1)) * n_kp + kp];
-      bf16x8 kop[2][4];
+      // every operand read of the step is issued up front
+      bf16x8 kop[2][4], vop[2][2][2];
       read_k(tn, 0, kop[0]);
       read_k(tn, 1, kop[1]);
-      // P V of tile j-1 while the probabilities of tile j are formed
-      pv(0, vop[0], pop);
-      pv(1, vop[1], pop);
-      probs(s, 0.f, pop);
       read_v(tc, 0, vop[0]);
       read_v(tc, 1, vop[1]);
+      // probabilities of tile j against the running maximum
+      bf16x8 pop[2];
+      probs(sc, 0.f, pop);
       // scores of tile j+1, relative to the running maximum
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kh][jj], qop[4 * kh + jj], kh == 0 && jj == 0 ? negm : s, 0, 0, 0);
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kh][jj], qop[4 * kh + jj], kh == 0 && jj == 0 ? negm : sn, 0, 0, 0);
+      pv(0, vop[0], pop);
+      pv(1, vop[1], pop);
       // maximum of tile j+1; the reference moves when it exceeds the slack
-      float x0 = max3f(s[0], s[1], s[2]), x1 = max3f(s[3], s[4], s[5]);
-      float x2 = max3f(s[6], s[7], s[8]), x3 = max3f(s[9], s[10], s[11]);
-      float x4 = max3f(s[12], s[13], s[14]);
+      float x0 = max3f(sn[0], sn[1], sn[2]), x1 = max3f(sn[3], sn[4], sn[5]);
+      float x2 = max3f(sn[6], sn[7], sn[8]), x3 = max3f(sn[9], sn[10], sn[11]);
+      float x4 = max3f(sn[12], sn[13], sn[14]);
       x0 = max3f(x0, x1, x2);
-      x3 = max3f(x3, x4, s[15]);
+      x3 = max3f(x3, x4, sn[15]);
       x0 = max2f(x0, x3);
       float y0, y1;
       halves(x0, y0, y1);
       const float tmax = max2f(y0, y1);
       const bool grow = tmax > kRescaleSlack;
       if (__ballot(grow)) {
-        // tile j's P V is still pending against the old reference: add it now, rescale,
-        // and leave zeros for the next step to add
-        pv(0, vop[0], pop);
-        pv(1, vop[1], pop);
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pop[t2][e] = static_cast<bf16>(0.0f);
         const float shift = grow ? tmax : 0.f;
         const float corr = exp2_fast(-shift);
         l_run *= corr;
@@ -823,15 +794,21 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
         m_run += shift;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          s[e] -= shift;
+          sn[e] -= shift;
           negm[e] = -m_run;
         }
       }
     };
-    for (; i < hot_end; ++i) steady(i, s_cur);
-    // the last pending P V
-    pv(0, vop[0], pop);
-    pv(1, vop[1], pop);
+    // unrolled twice so that the two score tiles trade places without copies
+    for (; i + 2 <= hot_end; i += 2) {
+      steady(i, s_cur, s_nxt);
+      steady(i + 1, s_nxt, s_cur);
+    }
+    if (i < hot_end) {
+      steady(i, s_cur, s_nxt);
+      s_cur = s_nxt;
+      ++i;
+    }
     // back to absolute scores for the general steps
 #pragma unroll
     for (int e = 0; e < 16; ++e) s_cur[e] += m_run;
@@ -916,28 +893,36 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
 // once per split.
 constexpr int kMergeGroup = 8;
 
+// Grid: x = unit, y = query block, z = 16-row chunk of the query block, so that every
+// index comes from the launch coordinates without a division by a run-time value.
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   const bool failed = round_failed(p.status);  // gates the store only
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int d8 = int(idx & 15);
-  const int64_t g = idx >> 4;  // (unit, query block, row of the block)
-  const int r = int(g % p.qrows);
-  const int64_t uq = g / p.qrows;
-  const int qb = int(uq % p.qblocks);
-  const int unit = int(uq / p.qblocks);
+  const int d8 = threadIdx.x & 15;
+  const int r = int(blockIdx.z) * 16 + (threadIdx.x >> 4);  // row of the query block
+  const int qb = int(blockIdx.y), unit = int(blockIdx.x);
   const int row = qb * p.qrows + r;
-  if (row >= p.rows) return;
-  const int64_t base = uq * p.splits * p.qrows + r;  // slot of split 0
+  if (r >= p.qrows || row >= p.rows) return;
+  const int64_t base = (int64_t(unit) * p.qblocks + qb) * p.splits * p.qrows + r;  // slot of split 0
   float M = -INFINITY, L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < p.splits; s0 += kMergeGroup) {
-    float2 ml[kMergeGroup];
-    uint4 v[kMergeGroup];
+    // issued as inline assembly, all sixteen loads back to back and then one wait: left to
+    // itself the compiler waits for each split's load before it issues the next
+    u32x2 mlw[kMergeGroup];
+    u32x4 v[kMergeGroup];
 #pragma unroll
     for (int k = 0; k < kMergeGroup; ++k) {  // slots past the last split re-read split 0
       const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
-      ml[k] = p.ml[slot];
-      v[k] = *reinterpret_cast<const uint4*>(p.o + slot * kD + 8 * d8);
+      mlw[k] = load_b64(p.ml + slot);
+      v[k] = load_b128(p.o + slot * kD + 8 * d8);
+    }
+    wait_vm(0);
+    float2 ml[kMergeGroup];
+#pragma unroll
+    for (int k = 0; k < kMergeGroup; ++k) {
+      pin(mlw[k]);
+      pin(v[k]);
+      ml[k] = make_float2(__uint_as_float(mlw[k][0]), __uint_as_float(mlw[k][1]));
     }
     float Mg = M;
 #pragma unroll
@@ -960,8 +945,9 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   }
   if (failed) return;
   const float inv = 1.0f / L;
-  const int b = unit / p.Hkv, kvh = unit % p.Hkv;
-  const int u = row / p.group, h = kvh * p.group + row % p.group;
+  const int b = unit / p.Hkv, kvh = unit - b * p.Hkv;
+  const uint32_t u = uint32_t(row) / uint32_t(p.group);
+  const int h = kvh * p.group + (row - int(u) * p.group);
   bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kD + 8 * d8;
   bf16x8 ov;
 #pragma unroll
@@ -1013,9 +999,9 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   m.qrows = plan.qrows;
   m.qblocks = plan.qblocks;
   m.splits = plan.splits;
-  const int64_t threads = int64_t(plan.units) * plan.qblocks * plan.qrows * 16;
   return launch(reinterpret_cast<const void*>(&tree_attn_merge_kernel),
-                dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, m, nullptr, ev_stop);
+                dim3(unsigned(plan.units), unsigned(plan.qblocks), unsigned((plan.qrows + 15) / 16)),
+                dim3(256), 0, stream, m, nullptr, ev_stop);
 }
 
 }  // namespace medusa
