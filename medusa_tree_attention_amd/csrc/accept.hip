@@ -101,10 +101,26 @@ __device__ __forceinline__ void keep_better(float& v, int& i, float ov, int oi) 
   }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// a 16-byte load whose completion the compiler does not track: the caller waits with an
+// explicit s_waitcnt and keeps the uses below it
+__device__ __forceinline__ f32x4 load_f32x4(const void* p) {
+  f32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+// maximum of two floats without the canonicalising moves fmaxf adds
+__device__ __forceinline__ float vmax(float x, float y) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+
 constexpr int kArgmaxThreads = 256;
 constexpr int kArgmaxUnroll = 8;  // 16-byte loads each thread has in flight
 constexpr int kMaxParts = 16;     // pieces per row at most
 constexpr size_t kSelectLds = 65536;  // bytes of tree buffers, candidates and targets
+constexpr int kHiddenRegs = 4;         // 16-byte hidden-state chunks per thread held in registers
 
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(AcceptArgs a) {
   // the status gates the stores only: its load overlaps the logits stream
@@ -122,29 +138,61 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(AcceptArgs a) {
   };
   const bool vec = (a.V % 4 == 0) && ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
   if (vec) {
-    // float4 columns [lo, hi) of the row; all kArgmaxUnroll loads of a pass are issued
-    // before any is compared, and loads past hi read column lo again (in bounds) and are
-    // not compared
+    // float4 columns [lo, hi) of the row.  The kArgmaxUnroll loads of a pass are issued
+    // back to back as inline assembly and waited for once (the compiler would otherwise
+    // wait for some before issuing the rest); loads past hi read column lo again (in
+    // bounds) and are not compared.  A pass is reduced without branches: its maximum over
+    // the valid values (v_max_f32 leaves a quiet NaN operand out; NaNs are flagged on the
+    // side and fail the round), then the lowest index holding that maximum, then one
+    // comparison with the running pair.
     const float4* row4 = reinterpret_cast<const float4*>(row);
     const int n4 = a.V / 4;
     const int lo = min(n4, piece * a.chunk4), hi = min(n4, lo + a.chunk4);
     for (int c0 = lo + int(threadIdx.x); c0 < hi; c0 += kArgmaxThreads * kArgmaxUnroll) {
-      float4 x[kArgmaxUnroll];
+      f32x4 x[kArgmaxUnroll];
 #pragma unroll
       for (int k = 0; k < kArgmaxUnroll; ++k) {
         const int c = c0 + k * kArgmaxThreads;
-        x[k] = row4[c < hi ? c : lo];
+        x[k] = load_f32x4(row4 + (c < hi ? c : lo));
       }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int k = 0; k < kArgmaxUnroll; ++k) {
-        const int c = c0 + k * kArgmaxThreads;
-        if (c < hi) {
-          take(x[k].x, 4 * c);
-          take(x[k].y, 4 * c + 1);
-          take(x[k].z, 4 * c + 2);
-          take(x[k].w, 4 * c + 3);
+      for (int k = 0; k < kArgmaxUnroll; ++k) asm volatile("" : "+v"(x[k]));
+      float pm = -INFINITY;
+      bool pnan = false;
+      int pi = INT_MAX;
+      if (c0 + (kArgmaxUnroll - 1) * kArgmaxThreads < hi) {  // the whole pass is in range
+#pragma unroll
+        for (int k = 0; k < kArgmaxUnroll; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pnan |= x[k][j] != x[k][j];
+            pm = vmax(pm, x[k][j]);
+          }
+#pragma unroll
+        for (int k = kArgmaxUnroll - 1; k >= 0; --k)
+#pragma unroll
+          for (int j = 3; j >= 0; --j) pi = x[k][j] == pm ? 4 * (c0 + k * kArgmaxThreads) + j : pi;
+      } else {
+#pragma unroll
+        for (int k = 0; k < kArgmaxUnroll; ++k) {
+          const bool ok = c0 + k * kArgmaxThreads < hi;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float e = ok ? x[k][j] : -INFINITY;
+            pnan |= e != e;
+            pm = vmax(pm, e);
+          }
+        }
+#pragma unroll
+        for (int k = kArgmaxUnroll - 1; k >= 0; --k) {
+          const int c = c0 + k * kArgmaxThreads;
+#pragma unroll
+          for (int j = 3; j >= 0; --j) pi = (c < hi && x[k][j] == pm) ? 4 * c + j : pi;
         }
       }
+      nan = nan || pnan;
+      if (pi != INT_MAX) keep_better(best, idx, pm, pi);
     }
   } else {
     const int chunk = (a.V + a.parts - 1) / a.parts;
@@ -311,6 +359,9 @@ template <bool kStaged, bool kTypical, bool kCommit = false>
 __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
   const bool failed = round_failed(a.status);  // gates the stores only
   const int b = blockIdx.x;
+  // the committed length is read with the first loads, not after the path walk: only this
+  // block writes it, at the very end
+  const int64_t P = kCommit ? a.prefix_len[b] : 0;
   extern __shared__ int32_t sm[];  // tgt[N], tix[N], cand[n_slots], ret[n_paths][W]
   const int32_t* tix = a.tree_indices;
   const int32_t* cand = a.candidates + int64_t(b) * a.n_slots;
@@ -320,12 +371,45 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
     int32_t* s_tix = s_tgt + a.N;
     int32_t* s_cand = s_tix + a.N;
     int32_t* s_ret = s_cand + a.n_slots;
-    for (int u = threadIdx.x; u < a.N; u += blockDim.x) {
+    // The first blockDim.x entries of every array come in one batch: each thread loads
+    // its entry of each (an index past the end is clamped, in bounds, and not stored) and
+    // all the piece results of its row's target, and nothing is stored to LDS before all
+    // of them are issued.  Larger arrays finish in the loops after.
+    const int t = int(threadIdx.x), nret = a.n_paths * a.W;
+    const int tu = min(t, a.N - 1);
+    const int32_t v_tix = tix[tu];
+    const int32_t v_cand = cand[min(t, a.n_slots - 1)];
+    const int32_t v_ret = ret[min(t, nret - 1)];
+    int32_t v_tgt = 0;
+    if (!kTypical) {
+      const int64_t row = int64_t(b) * a.N + tu;
+      if (a.logits) {
+        const int2* pr = a.part + row * a.parts;
+        int2 pv[kMaxParts];
+#pragma unroll
+        for (int k = 0; k < kMaxParts; ++k) pv[k] = pr[min(k, a.parts - 1)];
+        float v = __int_as_float(pv[0].x);
+        int i = pv[0].y;
+#pragma unroll
+        for (int k = 1; k < kMaxParts; ++k)
+          if (k < a.parts) keep_better(v, i, __int_as_float(pv[k].x), pv[k].y);
+        v_tgt = i;
+      } else {
+        v_tgt = a.target_ids[row];
+      }
+    }
+    if (t < a.N) {
+      if (!kTypical) s_tgt[t] = v_tgt;
+      s_tix[t] = v_tix;
+    }
+    if (t < a.n_slots) s_cand[t] = v_cand;
+    if (t < nret) s_ret[t] = v_ret;
+    for (int u = t + int(blockDim.x); u < a.N; u += blockDim.x) {
       if (!kTypical) s_tgt[u] = row_target(a, b, u);
       s_tix[u] = tix[u];
     }
-    for (int i = threadIdx.x; i < a.n_slots; i += blockDim.x) s_cand[i] = cand[i];
-    for (int i = threadIdx.x; i < a.n_paths * a.W; i += blockDim.x) s_ret[i] = ret[i];
+    for (int i = t + int(blockDim.x); i < a.n_slots; i += blockDim.x) s_cand[i] = cand[i];
+    for (int i = t + int(blockDim.x); i < nret; i += blockDim.x) s_ret[i] = ret[i];
     __syncthreads();
     tix = s_tix;
     cand = s_cand;
@@ -426,12 +510,23 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
     a.frontier[b] = r[alen];
   }
   if (kCommit) {
-    const int64_t P = a.prefix_len[b];  // only this block writes it, after the reads below
     const int G = alen + 1;
+    const int fr = r[alen];
+    // the terminal row's hidden state is loaded together with the cache rows below (the
+    // first kHiddenRegs 16-byte chunks per thread; longer states finish afterwards)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const unsigned char* hs = a.hidden + (int64_t(b) * a.N + fr) * a.hidden_bytes;
+    unsigned char* hd = a.h_next + int64_t(b) * a.hidden_bytes;
+    const int hchunks = a.h_next ? int(a.hidden_bytes >> 4) : 0;
+    u32x4 hv[kHiddenRegs];
+#pragma unroll
+    for (int k = 0; k < kHiddenRegs; ++k) {
+      const int i = int(threadIdx.x) + k * int(blockDim.x);
+      if (i < hchunks) hv[k] = *reinterpret_cast<const u32x4*>(hs + 16 * i);
+    }
     int32_t src[kCommitWidth];
 #pragma unroll
     for (int j = 0; j < kCommitWidth; ++j) src[j] = r[j < G ? j : 0];
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int cpr = a.row_bytes >> 4;  // 16-byte columns per row
     const int per_layer = a.Hkv * 2 * cpr;
     const int items = a.n_layers * per_layer;
@@ -451,13 +546,13 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
       for (int j = 0; j < kCommitWidth; ++j)
         if (j < G) *reinterpret_cast<u32x4*>(base + int64_t(j) * a.row_bytes) = v[j];
     }
-    const int fr = r[alen];
-    if (a.h_next) {  // the hidden state of the terminal row
-      const unsigned char* hs = a.hidden + (int64_t(b) * a.N + fr) * a.hidden_bytes;
-      unsigned char* hd = a.h_next + int64_t(b) * a.hidden_bytes;
-      for (int i = threadIdx.x; i < (a.hidden_bytes >> 4); i += blockDim.x)
-        *reinterpret_cast<u32x4*>(hd + 16 * i) = *reinterpret_cast<const u32x4*>(hs + 16 * i);
+#pragma unroll
+    for (int k = 0; k < kHiddenRegs; ++k) {
+      const int i = int(threadIdx.x) + k * int(blockDim.x);
+      if (i < hchunks) *reinterpret_cast<u32x4*>(hd + 16 * i) = hv[k];
     }
+    for (int i = int(threadIdx.x) + kHiddenRegs * int(blockDim.x); i < hchunks; i += blockDim.x)
+      *reinterpret_cast<u32x4*>(hd + 16 * i) = *reinterpret_cast<const u32x4*>(hs + 16 * i);
     __syncthreads();  // every thread has read P
     if (threadIdx.x == 0) {
       if (a.next_root) a.next_root[b] = tgt(fr);
