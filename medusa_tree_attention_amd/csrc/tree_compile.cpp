@@ -21,7 +21,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
-#include <map>
+#include <climits>
 #include <queue>
 #include <vector>
 
@@ -33,24 +33,45 @@ constexpr int32_t kMaxNodes = 16384;  // mask alone is N*N/8 bytes (32 MiB here)
 
 using Path = std::vector<int32_t>;
 
-struct Frontier {
+// A path of the greedy search, stored once in a pool as (parent, last rank): the frontier
+// holds pool ids, so a push copies no path.
+struct PoolNode {
+  int32_t parent;  // pool id, -1 for the root's children
+  int32_t rank;
+  int32_t depth;
   double w;
-  Path p;
 };
 
+// ranks of a pool path from the root down, into r[0 .. depth)
+void ranks_of(const std::vector<PoolNode>& pool, int32_t id, int32_t* r) {
+  for (int32_t v = id; v >= 0; v = pool[v].parent) r[pool[v].depth - 1] = pool[v].rank;
+}
+
 // Priority of the greedy loop: larger weight first, then the shorter path,
-// then the lexicographically smaller one.
+// then the lexicographically smaller one.  Only exact weight ties compare paths.
 struct LowerPriority {
-  bool operator()(const Frontier& a, const Frontier& b) const {
-    if (a.w != b.w) return a.w < b.w;
-    if (a.p.size() != b.p.size()) return a.p.size() > b.p.size();
-    return a.p > b.p;
+  const std::vector<PoolNode>* pool;
+  bool operator()(int32_t a, int32_t b) const {
+    const PoolNode& x = (*pool)[a];
+    const PoolNode& y = (*pool)[b];
+    if (x.w != y.w) return x.w < y.w;
+    if (x.depth != y.depth) return x.depth > y.depth;
+    int32_t ra[64], rb[64];  // depth <= num_heads <= 64
+    ranks_of(*pool, a, ra);
+    ranks_of(*pool, b, rb);
+    return std::lexicographical_compare(rb, rb + y.depth, ra, ra + x.depth);
   }
 };
 
 bool canonical_less(const Path& a, const Path& b) {
   if (a.size() != b.size()) return a.size() < b.size();
   return a < b;
+}
+
+// canonical order of a stored path against the first n ranks of another
+bool canonical_less_prefix(const Path& a, const int32_t* b, size_t n) {
+  if (a.size() != n) return a.size() < n;
+  return std::lexicographical_compare(a.begin(), a.end(), b, b + n);
 }
 
 // Number of rank tuples of length 1..K, saturated at `cap`.
@@ -74,22 +95,33 @@ medusa_status grow_greedy(const medusa_tree_spec& s, std::vector<Path>& paths,
   if (s.n_nodes > kMaxNodes) return MEDUSA_ECAPACITY;
   const int64_t budget = int64_t(s.n_nodes) - 1;
   if (budget > tuple_count(K, topk, int64_t(1) << 40)) return MEDUSA_ECAPACITY;
+  // every admitted path adds at most topk pool entries, addressed by int32 ids
+  if ((budget + 1) * int64_t(topk) > int64_t(INT32_MAX)) return MEDUSA_ECAPACITY;
 
-  std::priority_queue<Frontier, std::vector<Frontier>, LowerPriority> frontier;
-  for (int32_t r = 0; r < topk; ++r) frontier.push({1.0 * s.rank_hit[r], Path{r}});
+  std::vector<PoolNode> pool;
+  pool.reserve(size_t(std::min<int64_t>(budget, 1 << 20)) * size_t(topk) + size_t(topk));
+  std::vector<int32_t> heap_store;
+  heap_store.reserve(pool.capacity());
+  std::priority_queue<int32_t, std::vector<int32_t>, LowerPriority> frontier(LowerPriority{&pool},
+                                                                              std::move(heap_store));
+  for (int32_t r = 0; r < topk; ++r) {
+    pool.push_back({-1, r, 1, 1.0 * s.rank_hit[r]});
+    frontier.push(int32_t(pool.size()) - 1);
+  }
+  int32_t buf[64];
   while (int64_t(paths.size()) < budget) {
-    Frontier best = frontier.top();
+    const int32_t best = frontier.top();
     frontier.pop();
-    const int32_t depth = int32_t(best.p.size());
-    if (depth < K) {
+    const PoolNode node = pool[best];
+    if (node.depth < K) {
       for (int32_t r = 0; r < topk; ++r) {
-        Path child = best.p;
-        child.push_back(r);
-        frontier.push({best.w * s.rank_hit[int64_t(depth) * topk + r], std::move(child)});
+        pool.push_back({best, r, node.depth + 1, node.w * s.rank_hit[int64_t(node.depth) * topk + r]});
+        frontier.push(int32_t(pool.size()) - 1);
       }
     }
-    paths.push_back(std::move(best.p));
-    if (weights) weights->push_back(best.w);
+    ranks_of(pool, best, buf);
+    paths.emplace_back(buf, buf + node.depth);
+    if (weights) weights->push_back(node.w);
   }
   return MEDUSA_OK;
 }
@@ -128,21 +160,25 @@ extern "C" medusa_status medusa_tree_compile(const medusa_tree_spec* spec, medus
   }
   if (st != MEDUSA_OK) return st;
 
-  // canonical order, duplicates, prefix closure
+  // canonical order, duplicates, prefix closure: row u holds paths[u - 1], and the parent
+  // of a path is found by binary search for its prefix among the sorted paths
   std::sort(paths.begin(), paths.end(), canonical_less);
-  std::map<Path, int32_t> row;
-  row[Path{}] = 0;
-  for (size_t i = 0; i < paths.size(); ++i) {
-    if (!row.emplace(paths[i], int32_t(i + 1)).second) return MEDUSA_EINVAL;
-  }
+  for (size_t i = 1; i < paths.size(); ++i)
+    if (paths[i] == paths[i - 1]) return MEDUSA_EINVAL;
   const int32_t n = int32_t(paths.size()) + 1;
   std::vector<int32_t> parent(n, -1), depth(n, 0), slot(n, 0);
   for (int32_t u = 1; u < n; ++u) {
     const Path& p = paths[u - 1];
-    Path pre(p.begin(), p.end() - 1);
-    auto it = row.find(pre);
-    if (it == row.end()) return MEDUSA_ENOT_PREFIX_CLOSED;
-    parent[u] = it->second;
+    const size_t L = p.size() - 1;  // prefix length
+    if (L == 0) {
+      parent[u] = 0;
+    } else {
+      auto it = std::lower_bound(paths.begin(), paths.end(), p.data(),
+                                 [L](const Path& x, const int32_t* b) { return canonical_less_prefix(x, b, L); });
+      if (it == paths.end() || it->size() != L || !std::equal(it->begin(), it->end(), p.begin()))
+        return MEDUSA_ENOT_PREFIX_CLOSED;
+      parent[u] = int32_t(it - paths.begin()) + 1;
+    }
     depth[u] = int32_t(p.size());
     slot[u] = 1 + (depth[u] - 1) * s.topk + p.back();
   }
