@@ -57,7 +57,7 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeCache = 8;    // list keys per merge thread held in registers
 constexpr int kMaxTopk = 64;
 constexpr int kMaxD = 8192;
-constexpr int kTargetWaves = 256 * 16;  // 16 wavefronts on each of 256 compute units
+constexpr int kSplitBelow = 256 * 8;    // row groups are shared only below 8 per compute unit
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -440,10 +440,13 @@ __global__ __launch_bounds__(kMergeThreads) void head_topk_merge_kernel(TopkArgs
   if (tid == 0 && k == 0 && !failed) cand[0] = a.root[b];
 }
 
-// Launch shape of one GEMV over R rows: row groups of 8; with fewer groups than wavefronts
-// to fill the chip, 2..8 wavefronts share a group (each taking every split-th column of
-// pieces), one group per wavefront; otherwise about per_cu workgroups per compute unit and
-// head, each over a contiguous row range (at most max_rows rows, a multiple of 64).
+// Launch shape of one GEMV over R rows: row groups of 8; with fewer groups than half the
+// wavefront slots of the chip, 2..8 wavefronts share a group (each taking every split-th
+// column of pieces), one group per wavefront; otherwise about per_cu workgroups per compute
+// unit and head, each over a contiguous row range (at most max_rows rows, a multiple of 64).
+// Long streams per wavefront beat full occupancy here: the residual product at hidden 4096
+// (2048 groups) runs 30 us with one wavefront of 8 steps per group against 36 us with two
+// wavefronts of 4 steps each.
 struct GemvShape {
   int32_t split, rows_per_block, blocks;
 };
@@ -453,7 +456,7 @@ GemvShape gemv_shape(int32_t R, int32_t K, int32_t dpad, int32_t per_cu, int32_t
   const int64_t groups = int64_t(K) * ((R + kGemvRows - 1) / kGemvRows);
   const int32_t nch = dpad / kPad;
   sh.split = 1;
-  while (sh.split < kGemvWaves && sh.split * 2 <= nch && groups * sh.split < kTargetWaves) sh.split *= 2;
+  while (sh.split < kGemvWaves && sh.split * 2 <= nch && groups * sh.split < kSplitBelow) sh.split *= 2;
   if (sh.split > 1) {
     sh.rows_per_block = (kGemvWaves / sh.split) * kGemvRows;
   } else {
