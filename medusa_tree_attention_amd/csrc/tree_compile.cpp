@@ -22,6 +22,7 @@
 #include <cstdint>
 #include <cstring>
 #include <climits>
+#include <new>
 #include <queue>
 #include <vector>
 
@@ -99,9 +100,12 @@ medusa_status grow_greedy(const medusa_tree_spec& s, std::vector<Path>& paths,
   if ((budget + 1) * int64_t(topk) > int64_t(INT32_MAX)) return MEDUSA_ECAPACITY;
 
   std::vector<PoolNode> pool;
-  pool.reserve(size_t(std::min<int64_t>(budget, 1 << 20)) * size_t(topk) + size_t(topk));
+  // a modest reservation; larger searches grow the vectors (an allocation failure is
+  // reported as MEDUSA_ECAPACITY by the entry points)
+  const size_t want = size_t(std::min<int64_t>((budget + 1) * int64_t(topk), int64_t(1) << 16));
+  pool.reserve(want);
   std::vector<int32_t> heap_store;
-  heap_store.reserve(pool.capacity());
+  heap_store.reserve(want);
   std::priority_queue<int32_t, std::vector<int32_t>, LowerPriority> frontier(LowerPriority{&pool},
                                                                               std::move(heap_store));
   for (int32_t r = 0; r < topk; ++r) {
@@ -145,7 +149,7 @@ medusa_status read_explicit(const medusa_tree_spec& s, std::vector<Path>& paths)
 
 }  // namespace
 
-extern "C" medusa_status medusa_tree_compile(const medusa_tree_spec* spec, medusa_tree* out) {
+static medusa_status tree_compile_impl(const medusa_tree_spec* spec, medusa_tree* out) {
   if (spec == nullptr || out == nullptr) return MEDUSA_EINVAL;
   const medusa_tree_spec& s = *spec;
   if (s.num_heads < 1 || s.topk < 1 || s.num_heads > 64) return MEDUSA_EINVAL;
@@ -254,10 +258,9 @@ extern "C" medusa_status medusa_tree_compile(const medusa_tree_spec* spec, medus
 // node count changes with context length.  The tree of budget N is the first N - 1
 // admissions of the greedy growth, so E[A](N) is their weights' running sum (admission
 // order, binary64), and the round rate is (1 + E[A](N)) / (fixed_us + n_layers * t(N)).
-extern "C" medusa_status medusa_tree_budget(const double* rank_hit, int32_t num_heads, int32_t topk,
-                                            int32_t n_costs, const int32_t* cost_nodes,
-                                            const double* cost_us, double fixed_us, int32_t n_layers,
-                                            int32_t* best_n, double* expected_tokens, double* rate) {
+static medusa_status tree_budget_impl(const double* rank_hit, int32_t num_heads, int32_t topk, int32_t n_costs,
+                                      const int32_t* cost_nodes, const double* cost_us, double fixed_us,
+                                      int32_t n_layers, int32_t* best_n, double* expected_tokens, double* rate) {
   if (!rank_hit || !cost_nodes || !cost_us || !best_n || num_heads < 1 || topk < 1 || n_costs < 1 ||
       n_layers < 0 || !(fixed_us >= 0.0) || !std::isfinite(fixed_us))
     return MEDUSA_EINVAL;
@@ -304,4 +307,30 @@ extern "C" medusa_status medusa_tree_budget(const double* rank_hit, int32_t num_
   if (rate) rate[0] = 0.0;
   *best_n = best;
   return MEDUSA_OK;
+}
+
+// C entry points: no exception crosses the ABI (an allocation failure of a very large
+// search or tree is reported as MEDUSA_ECAPACITY)
+extern "C" medusa_status medusa_tree_compile(const medusa_tree_spec* spec, medusa_tree* out) {
+  try {
+    return tree_compile_impl(spec, out);
+  } catch (const std::bad_alloc&) {
+    return MEDUSA_ECAPACITY;
+  } catch (...) {
+    return MEDUSA_EINVAL;
+  }
+}
+
+extern "C" medusa_status medusa_tree_budget(const double* rank_hit, int32_t num_heads, int32_t topk,
+                                            int32_t n_costs, const int32_t* cost_nodes,
+                                            const double* cost_us, double fixed_us, int32_t n_layers,
+                                            int32_t* best_n, double* expected_tokens, double* rate) {
+  try {
+    return tree_budget_impl(rank_hit, num_heads, topk, n_costs, cost_nodes, cost_us, fixed_us, n_layers,
+                            best_n, expected_tokens, rate);
+  } catch (const std::bad_alloc&) {
+    return MEDUSA_ECAPACITY;
+  } catch (...) {
+    return MEDUSA_EINVAL;
+  }
 }
