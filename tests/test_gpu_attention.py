@@ -159,3 +159,30 @@ def test_running_maximum_moves_inside_the_key_stream():
     err, staged = run.check(sample_rows(w, N, 96, seed=2, must=must))
     announce(f"  max abs err {err:.3e}")
     assert err <= TOL[w.dtype] and staged <= 1.0
+
+
+def test_deepest_supported_chain_and_the_first_unsupported_depth():
+    """The matrix-core path keeps RoPE phases for depths 0..31.  A chain 31 deep (32 rows,
+    positions P .. P + 31) must verify like causal attention over the prefix and the path;
+    a chain 32 deep must fail the round on the device with MEDUSA_EUNSUPPORTED and store
+    nothing to the cache or the output."""
+    base = dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=8, Hkv=2, tree="cartesian", topk=1)
+    w = dataclasses.replace(base, branching=(1,) * 31, num_heads=31)
+    announce("attention: a 31-deep chain (the deepest RoPE phase kept)")
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w, seed=41, prefix_len=[300, 1000])
+    run = AttnRun(w, x, lib, ora)
+    assert run.run() == 0
+    err, staged = run.check(_all_rows(w, x["N"]))
+    announce(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.dtype] and staged <= 1.0
+
+    w = dataclasses.replace(base, branching=(1,) * 32, num_heads=32)
+    announce("attention: a 32-deep chain is rejected on the device")
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w, seed=42, prefix_len=[300, 1000])
+    run = AttnRun(w, x, lib, ora)
+    kc0, vc0, out0 = host(run.kc).copy(), host(run.vc).copy(), host(run.out).copy()
+    assert run.run() == -4  # MEDUSA_EUNSUPPORTED
+    assert np.array_equal(host(run.kc), kc0) and np.array_equal(host(run.vc), vc0)
+    assert np.array_equal(host(run.out), out0)
