@@ -186,3 +186,30 @@ def test_deepest_supported_chain_and_the_first_unsupported_depth():
     assert run.run() == -4  # MEDUSA_EUNSUPPORTED
     assert np.array_equal(host(run.kc), kc0) and np.array_equal(host(run.vc), vc0)
     assert np.array_equal(host(run.out), out0)
+
+
+def test_batch_of_more_than_64_sequences():
+    """70 sequences on the matrix-core path: the prefix lengths are checked 64 per pass, so a
+    sequence past the first 64 that does not fit must fail the round (no stores), and a
+    fitting batch must match the oracle on rows of sequences on both sides of 64."""
+    w = dataclasses.replace(workloads.WORKLOADS["batched"], B=70, Hq=4, Hkv=1, tree="cartesian",
+                            branching=(2, 2), num_heads=2, topk=2, slack=3)
+    announce("attention with 70 sequences")
+    lib, ora = compile_both(w)
+    rng = np.random.default_rng(43)
+    prefix = [int(p) for p in rng.integers(0, 250, size=w.B)]
+    x = workloads.draw_round(w, seed=43, prefix_len=prefix)
+    run = AttnRun(w, x, lib, ora)
+    assert run.run() == 0
+    N = x["N"]
+    must = [(b, u, h) for b in (0, 63, 64, 69) for u in (0, N - 1) for h in (0, w.Hq - 1)]
+    err, staged = run.check(sample_rows(w, N, 64, seed=3, must=must))
+    announce(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.dtype] and staged <= 1.0
+
+    x["prefix_len"] = x["prefix_len"].copy()
+    x["prefix_len"][67] = x["S_max"] - N + 1  # sequence 67 has no room for its staged rows
+    run = AttnRun(w, x, lib, ora)
+    kc0, out0 = host(run.kc).copy(), host(run.out).copy()
+    assert run.run() == -3  # MEDUSA_ECAPACITY
+    assert np.array_equal(host(run.kc), kc0) and np.array_equal(host(run.out), out0)

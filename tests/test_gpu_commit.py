@@ -230,3 +230,24 @@ def test_host_rejects_bad_arguments():
                                st["accept_len"], st["accepted_tokens"], st["frontier_row"], st["k"], st["v"],
                                st["prefix"], st["status"], logits=inp["logits"], workspace=inp["ws"][:16])
     unchanged(case, st, case.x["prefix_len"])
+
+
+def test_batch_of_more_than_64_sequences():
+    """Accept, commit and carry for 70 sequences against the oracle."""
+    w = dataclasses.replace(workloads.WORKLOADS["batched"], B=70, Hq=4, Hkv=1, tree="cartesian",
+                            branching=(2, 2), num_heads=2, topk=2, P=120, slack=5, vocab=512)
+    announce("accept+commit with 70 sequences")
+    case = CommitCase(w, 47, 2)
+    inp = case.inputs()
+    st = case.device_state()
+    assert case.run_fused(st, inp) == 0
+    got = host_state(st)
+    res, caches, new_len, carry = case.oracle()
+    for k in ("best_path", "accept_len", "frontier_row", "accepted_tokens"):
+        assert np.array_equal(got[k], res[k]), k
+    assert np.array_equal(got["prefix"], new_len)
+    for g, r in zip(got["caches"], caches):
+        assert np.array_equal(g, r)
+    assert np.array_equal(got["next_root"], carry["next_root"])
+    assert np.array_equal(got["h_next"], carry["h_next"].astype(np.float32))
+    announce(f"  accept lengths {np.bincount(got['accept_len']).tolist()}")
