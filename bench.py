@@ -311,8 +311,9 @@ def main():
                     help="acceptance rule of the round (typical: temperature 1, epsilon 0.3, alpha 0.09)")
     ap.add_argument("--commit", choices=["fused", "separate"], default="fused",
                     help="greedy rounds: accept and compact in one call (fused) or two")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the same number of steps replayed from one captured HIP graph")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the same number of steps replayed from one captured HIP graph "
+                         "(reported beside the eager figure, which stays the value)")
     ap.add_argument("--budget", action="store_true",
                     help="sweep the attention call over tree sizes and contexts and choose the node "
                          "budget per context (medusa_tree_budget); prints its own JSON line")
