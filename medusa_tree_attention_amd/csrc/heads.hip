@@ -58,6 +58,10 @@ constexpr int kMergeCache = 8;    // list keys per merge thread held in register
 constexpr int kMaxTopk = 64;
 constexpr int kMaxD = 8192;
 constexpr int kSplitBelow = 256 * 8;    // row groups are shared only below 8 per compute unit
+// cache policy of the weight loads: nontemporal (nt).  Every weight is read once per call;
+// marking the stream nontemporal took the unembedding product of the batched full round from
+// 191.5 to 175.2 us
+constexpr int kStreamLoad = 2;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -211,7 +215,7 @@ void head_gemv_kernel(GemvArgs g) {
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r) {
       const int rr = r < last ? r : last;
-      w[r] = __builtin_amdgcn_raw_buffer_load_b128(wres, voff, unsigned(rr) * unsigned(g.d) * 2u, 0);
+      w[r] = __builtin_amdgcn_raw_buffer_load_b128(wres, voff, unsigned(rr) * unsigned(g.d) * 2u, kStreamLoad);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the FMAs that follow
   };
