@@ -272,7 +272,9 @@ __global__ __launch_bounds__(kStatThreads) void typical_stats_kernel(AcceptArgs 
 #pragma unroll
       for (int k = 0; k < kStatCache / 4; ++k) {
         const int c = tid + k * kStatThreads;
-        const float4 x = row4[c < n4 ? c : 0];
+        // each logit is read once: a nontemporal load
+        const f32x4 x4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row4) + (c < n4 ? c : 0));
+        const float4 x = make_float4(x4[0], x4[1], x4[2], x4[3]);
         const bool in = c < n4;
         z[4 * k] = in ? x.x : -INFINITY;
         z[4 * k + 1] = in ? x.y : -INFINITY;
