@@ -44,6 +44,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix rate (published)
 ATTN_SOURCES = ["attn.hip", "attn_mfma.hip", "attn_common.h", "common.h"]
 HEAD_SOURCES = ["heads.hip", "common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_batched.md")
@@ -68,6 +69,12 @@ def attn_source_hash():
 
 def head_source_hash():
     return source_hash(HEAD_SOURCES)
+
+
+def algorithmic_flops(w, N):
+    """Matrix FLOPs of the attention call: Q K^T and P V over every committed and staged key,
+    4 d_h Hq N (P + N) B (the masked staged pairs included, as the matrix cores compute them)."""
+    return 4 * w.d * w.Hq * N * (w.P + N) * w.B
 
 
 def algorithmic_bytes(w, N, esize):
@@ -535,6 +542,11 @@ def main():
         "attention_nodes_per_s": w.B * N / mean_s,
         "tree_compile_us": compile_us,
     }
+    if w.dtype == "bf16":  # the matrix-core path; its peak is the dense bf16 MFMA rate
+        flops = algorithmic_flops(w, N)
+        result["mfma"] = {"achieved": flops / mean_s / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": flops / mean_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                          "flops": flops, "kernel": "medusa_tree_attn"}
     if heads is not None:
         h_alg = head_algorithmic_bytes(w.B, w.num_heads, hidden, w.vocab, w.topk)
         h_mean = float(head_ms.mean()) * 1e-3
