@@ -417,6 +417,10 @@ def main():
                 acc = (sptr, w.B, N, w.vocab, p(s["logits"]), 1.0, 0.3, 0.09, p(s["cand"]), n_slots,
                        p(shared["tidx"]), p(shared["retrieve"]), nn, width, p(s["best"]), p(s["alen"]),
                        p(s["tokens"]), p(s["frontier"]), p(s["acc_ws"]), s["acc_ws"].numel(), status)
+                # typical rounds commit with the separate compaction call
+                cmp_ = (sptr, dcode, 1, w.B, w.Hkv, w.d, x["S_max"], N, ctypes.cast(kc_arr, ctypes.c_void_p),
+                        ctypes.cast(vc_arr, ctypes.c_void_p), p(shared["retrieve"]), nn, width, p(s["best"]),
+                        p(s["alen"]), prefix, status)
             elif fused:
                 carry = ((hidden, p(hidden_rows), p(heads["h"]), p(heads["root"])) if hidden_rows is not None
                          else (0, None, None, None))
