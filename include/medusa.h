@@ -104,8 +104,9 @@ typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
  * Errors: MEDUSA_EINVAL (bad field, rank/length out of range, duplicate, rank_hit
  * outside [0,1] or NaN, n_nodes < 1), MEDUSA_ENOT_PREFIX_CLOSED, MEDUSA_ECAPACITY
  * (mode B: n_nodes-1 exceeds the number of rank tuples or n_nodes > 16384; mode
- * A: 16384 or more explicit paths, i.e. more than 16384 rows),
- * MEDUSA_EBUFSIZE.
+ * A: 16384 or more explicit paths, i.e. more than 16384 rows; either mode: host
+ * memory for the search or the tree runs out), MEDUSA_EBUFSIZE.  No exception
+ * leaves the call.
  */
 typedef struct {
   int32_t num_heads;           /* K: Medusa heads = maximum depth, >= 1 */
@@ -147,7 +148,8 @@ medusa_status medusa_tree_compile(const medusa_tree_spec* spec, medusa_tree* out
  * fixed_us is the tree-independent cost of a round (for example the backbone weight stream).
  * Errors: MEDUSA_EINVAL (NULL pointer, non-increasing or non-positive node counts, a negative
  * or non-finite cost, rank_hit outside [0, 1], a round that would cost nothing),
- * MEDUSA_ECAPACITY (more rows than the rank table can hold).  Host only.
+ * MEDUSA_ECAPACITY (more rows than the rank table can hold, or host memory for the search
+ * runs out).  Host only; no exception leaves the call.
  */
 medusa_status medusa_tree_budget(const double* rank_hit, int32_t num_heads, int32_t topk, int32_t n_costs,
                                  const int32_t* cost_nodes, const double* cost_us, double fixed_us,
