@@ -115,3 +115,34 @@ def test_vocab_not_multiple_of_four():
     status, got = AcceptRun(w, x, lib).run()
     assert status == 0
     _compare(got, oracle_accept(ora, x["candidates"], logits=x["logits"]))
+
+
+def test_argmax_ties_across_passes_and_threads():
+    """With 16 x 64 rows a row is one piece read by 256 threads in four passes of 8 float4
+    columns each (column c4 of pass p, slot k, thread t: c4 = t + 256 k + 2048 p; the last
+    pass is partial).  The root rows of three sequences hold two equal maxima, the higher
+    index being the token of tree row 1, the lower one read by the same thread in an earlier
+    pass, by the same thread in the same pass, or by another thread: the lower index must
+    win, so nothing is accepted through row 1."""
+    w = dataclasses.replace(workloads.WORKLOADS["llama7b"], B=16, vocab=32000)
+    announce("accept argmax ties across passes, slots and threads")
+    lib, ora = compile_both(w)
+    x = workloads.draw_round(w, seed=9)
+    slot1 = int(ora["tree_indices"][1])
+    hi = 30001                                 # float4 column 7500 = 76 + 256*5 + 2048*3, element 1
+    lows = [4 * (76 + 256 * 5) + 1,            # thread 76, pass 0: an earlier pass
+            4 * (6144 + 76) + 1,               # thread 76, pass 3, slot 0: the same pass
+            4 * (6144 + 6) + 1]                # thread 6, pass 3: another thread
+    lg = x["logits"]
+    for b, lo in enumerate(lows):
+        x["candidates"][b, slot1] = hi
+        depth1 = [int(x["candidates"][b, s]) for s in ora["tree_indices"][1:] if s <= w.topk]
+        assert lo not in depth1               # a wrong tie-break, not another child, decides
+        lg[b, 0, :] = -1.0
+        lg[b, 0, lo] = 5.0
+        lg[b, 0, hi] = 5.0
+    status, got = AcceptRun(w, x, lib).run()
+    assert status == 0
+    ref = oracle_accept(ora, x["candidates"], logits=x["logits"])
+    _compare(got, ref)
+    assert (ref["accept_len"][:3] == 0).all()
