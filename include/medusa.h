@@ -184,7 +184,7 @@ medusa_status medusa_tree_budget(const double* rank_hit, int32_t num_heads, int3
  * dt in {MEDUSA_F32, MEDUSA_BF16}.
  * Workspace: device memory of at least medusa_tree_attn_workspace_size(...)
  * bytes, owned by the caller.  For bf16 with d_h = 128 it receives the partial
- * results of the key-range splits ((m, l) in fp32 and O / l in bf16 per query
+ * results of the key-range splits ((m, l) and O / l in fp32 per query
  * row and split), merged into out by a second kernel of the same call; no state
  * carries from one call to the next.  Calls sharing a workspace must be ordered
  * (same stream).

@@ -32,6 +32,10 @@
 //    16-byte LDS reads), so the probability tile comes out of the accumulator
 //    already in the B-operand order of O^T = V^T P^T; V^T comes from LDS with
 //    the transposing ds_read_b64_tr_b16.  P is never shuffled.
+//  * The rotated, scaled query q~ is carried as two bf16 operands, hi = bf16(q~)
+//    and lo = bf16(q~ - hi), and each score is K hi + K lo.  One bf16 rounding of
+//    q~ alone moves a score by about 2^-9 |q~||k|, which a peaked softmax hands on
+//    to the output almost undamped; the pair is exact to about 2^-17.
 //  * Software pipeline per wavefront: the scores of tile j+1 are formed on the
 //    matrix core before the softmax of tile j.
 //  * Online softmax in log2 units; the running maximum only moves when a tile
@@ -47,7 +51,8 @@
 //    lane with the ancestor bitmask.  RoPE phases are reduced modulo 2 pi in
 //    binary64 and evaluated in fp32.
 //  * Splits of one query block are merged by a second, small kernel from
-//    (m, l, O) partials in the workspace; with a single split the first kernel
+//    (m, l, O / l) partials kept in fp32 in the workspace (a bf16 partial would add
+//    a second rounding to the output's); with a single split the first kernel
 //    writes the output itself.
 
 #include <cmath>
@@ -99,7 +104,7 @@ struct MfmaArgs {
 
 struct MergeArgs {
   const float2* ml;  // [units][qblocks][splits][qrows] (m, l)
-  const bf16* o;     // [units][qblocks][splits][qrows][D], O / l of the split
+  const float* o;    // [units][qblocks][splits][qrows][D], O / l of the split
   void* out;
   const int32_t* status;
   int32_t Hq, Hkv, N, group, rows, qrows, qblocks, splits;
@@ -130,7 +135,7 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
   p.xcd_map = p.qblocks > 1 && (int64_t(p.units) * p.splits) % 8 == 0;
   const size_t slots = size_t(p.units) * p.qblocks * p.splits * p.qrows;
   p.o_offset = (slots * sizeof(float2) + 255) / 256 * 256;
-  p.bytes = p.splits > 1 ? p.o_offset + slots * kD * sizeof(bf16) : 256;
+  p.bytes = p.splits > 1 ? p.o_offset + slots * kD * sizeof(float) : 256;
   return p;
 }
 
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // ---- this wavefront's 32 query rows: rotated, scaled to log2 units, bf16 B operands;
   // lane holds query column l32, dims 16 s + 8 half + e (e < 8)
   const float qscale = kLog2e / sqrtf(float(kD));
-  bf16x8 qop[8];
+  bf16x8 qhi[8], qlo[8];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const bf16x8 lo = __builtin_bit_cast(bf16x8, raw[s]);
@@ -475,8 +480,12 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     for (int e = 0; e < 8; ++e) {
       const float2 cs = s_cs[dep_q][16 * s + 8 * half + e];
       const float x1 = float(lo[e]), x2 = float(hi[e]);
-      qop[s][e] = static_cast<bf16>((x1 * cs.x - x2 * cs.y) * qscale);
-      qop[s + 4][e] = static_cast<bf16>((x2 * cs.x + x1 * cs.y) * qscale);
+      const float r1 = (x1 * cs.x - x2 * cs.y) * qscale;
+      const float r2 = (x2 * cs.x + x1 * cs.y) * qscale;
+      qhi[s][e] = static_cast<bf16>(r1);
+      qhi[s + 4][e] = static_cast<bf16>(r2);
+      qlo[s][e] = static_cast<bf16>(r1 - float(qhi[s][e]));
+      qlo[s + 4][e] = static_cast<bf16>(r2 - float(qhi[s + 4][e]));
     }
   }
 
@@ -548,7 +557,10 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       for (int e = 0; e < 16; ++e) s[e] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[j], qop[4 * kh + j], s, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[j], qhi[4 * kh + j], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[j], qlo[4 * kh + j], s, 0, 0, 0);
+    }
   };
   // visibility bits of a tile's 32 keys for this lane's query row (bit m = key m of the
   // tile); all ones for a full prefix tile
@@ -722,54 +734,65 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // staged-row fixes or variable waits, and their load addresses advance by a fixed
   // stride, so they run as a separate loop with as few instructions as possible.  The
   // remaining steps (the ring's drain, partial and staged tiles) take the general path.
-  const int hot_end = max(0, min(n_st - S + 1, (P / kTile) / n_kp - s_lo - S + 1));
+  // stages of this split whose tiles are all full prefix tiles; a step over two of them
+  // needs no masks, and while the stage it issues is one of them its loads advance by a
+  // fixed stride with a fixed wait; the ring's drain issues through issue_stage()
+  const int n_full = max(0, min(n_st, (P / kTile) / n_kp - s_lo));
+  const int fast_end = max(0, n_full - 1);
+  const int hot_end = max(0, n_full - S + 1);
   int i = 0;
-  if (hot_end > 0) {
-    // In the steady loop the score tiles are kept relative to the running maximum: the
-    // first score MFMA of a tile starts from the accumulator value -m_run, so exp2 takes
-    // the accumulator directly.  The running maximum is checked at the end of each step,
-    // on the scores just formed, and moved (rarely) before they are used.
+  if (fast_end > 0) {
+    // The running maximum is checked at the end of each step, on the scores just formed,
+    // and moved (rarely) before they are used.
     update_max(s_cur);
-    f32x16 negm;
+    f32x16 zero;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s_cur[e] -= m_run;
-      negm[e] = -m_run;
-    }
+    for (int e = 0; e < 16; ++e) zero[e] = 0.f;
     // global addresses of the tiles of stage S-1 (issued by step 0); lane offsets in poff[]
     const bf16* kq = kc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
     const bf16* vq = vc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
     const uint32_t ring0 = lds_addr(&s_ring[0][0]) + 256 * kDmaRows * wave;
-    auto steady = [&](int j, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteadyWait) : "memory");
-      __syncthreads();  // stage j+1 visible; every wavefront is done with stage j-1
-      const uint32_t dst = ring0 + uint32_t(((j + S - 1) & (S - 1)) * n_kp * kTileBytes);
+    auto steady = [&](int j, f32x16& sc, f32x16& sn, auto fixed) __attribute__((always_inline)) {
+      if constexpr (decltype(fixed)::value) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteadyWait) : "memory");
+        __syncthreads();  // stage j+1 visible; every wavefront is done with stage j-1
+        const uint32_t dst = ring0 + uint32_t(((j + S - 1) & (S - 1)) * n_kp * kTileBytes);
 #pragma unroll
-      for (int k = 0; k < n_kp; ++k)
+        for (int k = 0; k < n_kp; ++k)
 #pragma unroll
-        for (int h = 0; h < kDmaOps; ++h) {
-          dma16(kq + k * kTile * kD, poff[h], dst + k * kTileBytes + 1024 * h);
-          dma16(vq + k * kTile * kD, poff[h], dst + k * kTileBytes + 8192 + 1024 * h);
-        }
-      kq += n_kp * kTile * kD;
-      vq += n_kp * kTile * kD;
+          for (int h = 0; h < kDmaOps; ++h) {
+            dma16(kq + k * kTile * kD, poff[h], dst + k * kTileBytes + 1024 * h);
+            dma16(vq + k * kTile * kD, poff[h], dst + k * kTileBytes + 8192 + 1024 * h);
+          }
+        kq += n_kp * kTile * kD;
+        vq += n_kp * kTile * kD;
+      } else {
+        wait_stage(j + 1, min(j + S - 2, n_st - 1));
+        __syncthreads();
+        if (j + S - 1 < n_st) issue_stage(j + S - 1);
+      }
       const unsigned char* tn = s_ring[((j + 1) & (S - 1)) * n_kp + kp];
       const unsigned char* tc = s_ring[(j & (S - 1)) * n_kp + kp];
-      // every operand read of the step is issued up front
-      bf16x8 kop[2][4], vop[2][2][2];
-      read_k(tn, 0, kop[0]);
-      read_k(tn, 1, kop[1]);
+      // the operand reads of the step: the first half of the K operands and every V operand
+      // up front, the second half of the K operands once the first half is in use (the
+      // query rows, carried as a hi/lo pair, leave no room for all of them at once)
+      bf16x8 kop[4], vop[2][2][2];
+      read_k(tn, 0, kop);
       read_v(tc, 0, vop[0]);
       read_v(tc, 1, vop[1]);
       // probabilities of tile j against the running maximum
       bf16x8 pop[2];
-      probs(sc, 0.f, pop);
-      // scores of tile j+1, relative to the running maximum
+      probs(sc, m_run, pop);
+      // scores of tile j+1
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+      for (int kh = 0; kh < 2; ++kh) {
+        if (kh == 1) read_k(tn, 1, kop);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kh][jj], qop[4 * kh + jj], kh == 0 && jj == 0 ? negm : sn, 0, 0, 0);
+        for (int jj = 0; jj < 4; ++jj) {
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj], qhi[4 * kh + jj], kh == 0 && jj == 0 ? zero : sn, 0, 0, 0);
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj], qlo[4 * kh + jj], sn, 0, 0, 0);
+        }
+      }
       pv(0, vop[0], pop);
       pv(1, vop[1], pop);
       // maximum of tile j+1; the reference moves when it exceeds the slack
@@ -782,36 +805,32 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       float y0, y1;
       halves(x0, y0, y1);
       const float tmax = max2f(y0, y1);
-      const bool grow = tmax > kRescaleSlack;
+      const bool grow = tmax > m_run + kRescaleSlack;
       if (__ballot(grow)) {
-        const float shift = grow ? tmax : 0.f;
-        const float corr = exp2_fast(-shift);
+        const float m_new = grow ? tmax : m_run;
+        const float corr = exp2_fast(m_run - m_new);
         l_run *= corr;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
-        m_run += shift;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          sn[e] -= shift;
-          negm[e] = -m_run;
-        }
+        m_run = m_new;
       }
     };
     // unrolled twice so that the two score tiles trade places without copies
-    for (; i + 2 <= hot_end; i += 2) {
-      steady(i, s_cur, s_nxt);
-      steady(i + 1, s_nxt, s_cur);
-    }
-    if (i < hot_end) {
-      steady(i, s_cur, s_nxt);
-      s_cur = s_nxt;
-      ++i;
-    }
-    // back to absolute scores for the general steps
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s_cur[e] += m_run;
+    auto run = [&](int end, auto fixed) __attribute__((always_inline)) {
+      for (; i + 2 <= end; i += 2) {
+        steady(i, s_cur, s_nxt, fixed);
+        steady(i + 1, s_nxt, s_cur, fixed);
+      }
+      if (i < end) {
+        steady(i, s_cur, s_nxt, fixed);
+        s_cur = s_nxt;
+        ++i;
+      }
+    };
+    run(hot_end, std::true_type{});
+    run(fast_end, std::false_type{});
     b_cur = 0xffffffffu;  // the current tile is a full prefix tile
   }
   // the remaining steps: the end of the ring, partial and staged tiles
@@ -870,41 +889,40 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       }
     return;
   }
-  // partial of a split: (m, l) in fp32 and O / l rounded to bf16 (zero for a split that saw
-  // no key of the row)
+  // partial of a split: (m, l) and O / l in fp32 (zero for a split that saw no key of the row)
   const int64_t slot = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave + l32;
   if (half == 0) static_cast<float2*>(a.workspace)[slot] = make_float2(m_run, lsum);
-  bf16* po = reinterpret_cast<bf16*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kD + 4 * half;
+  float* po = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kD + 4 * half;
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x16& v = oacc[db];
-      const bf16x4 ov = {static_cast<bf16>(v[4 * g] * inv), static_cast<bf16>(v[4 * g + 1] * inv),
-                         static_cast<bf16>(v[4 * g + 2] * inv), static_cast<bf16>(v[4 * g + 3] * inv)};
-      *reinterpret_cast<bf16x4*>(po + 32 * db + 8 * g) = ov;
+      *reinterpret_cast<float4*>(po + 32 * db + 8 * g) =
+          make_float4(v[4 * g] * inv, v[4 * g + 1] * inv, v[4 * g + 2] * inv, v[4 * g + 3] * inv);
     }
 }
 
-// Merge of the splits: thread (row, 8 dims) combines the splits' partials, weighting split
+// Merge of the splits: thread (row, 4 dims) combines the splits' partials, weighting split
 // s by l_s 2^(m_s - M).  The splits are visited eight at a time with every load of a group
 // issued before any is used, so that a thread waits for memory once per group rather than
 // once per split.
 constexpr int kMergeGroup = 8;
+constexpr int kMergeRows = 8;  // query rows per 256-thread block
 
-// Grid: x = unit, y = query block, z = 16-row chunk of the query block, so that every
-// index comes from the launch coordinates without a division by a run-time value.
+// Grid: x = unit, y = query block, z = 8-row chunk of the query block, so that every index
+// comes from the launch coordinates without a division by a run-time value.
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   const bool failed = round_failed(p.status);  // gates the store only
-  const int d8 = threadIdx.x & 15;
-  const int r = int(blockIdx.z) * 16 + (threadIdx.x >> 4);  // row of the query block
+  const int d4 = threadIdx.x & 31;
+  const int r = int(blockIdx.z) * kMergeRows + (threadIdx.x >> 5);  // row of the query block
   const int qb = int(blockIdx.y), unit = int(blockIdx.x);
   const int row = qb * p.qrows + r;
   if (r >= p.qrows || row >= p.rows) return;
   const int64_t base = (int64_t(unit) * p.qblocks + qb) * p.splits * p.qrows + r;  // slot of split 0
   float M = -INFINITY, L = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < p.splits; s0 += kMergeGroup) {
     // issued as inline assembly, all sixteen loads back to back and then one wait: left to
     // itself the compiler waits for each split's load before it issues the next
@@ -914,7 +932,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
     for (int k = 0; k < kMergeGroup; ++k) {  // slots past the last split re-read split 0
       const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
       mlw[k] = load_b64(p.ml + slot);
-      v[k] = load_b128(p.o + slot * kD + 8 * d8);
+      v[k] = load_b128(p.o + slot * kD + 4 * d4);
     }
     wait_vm(0);
     float2 ml[kMergeGroup];
@@ -932,14 +950,13 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
     const float c = M == -INFINITY ? 0.f : exp2_fast(M - Mg);
     L *= c;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= c;
+    for (int e = 0; e < 4; ++e) acc[e] *= c;
 #pragma unroll
     for (int k = 0; k < kMergeGroup; ++k) {
       const float wt = (s0 + k < p.splits && ml[k].x != -INFINITY) ? ml[k].y * exp2_fast(ml[k].x - Mg) : 0.f;
-      const bf16x8 o8 = __builtin_bit_cast(bf16x8, v[k]);
       L += wt;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wt * float(o8[e]);
+      for (int e = 0; e < 4; ++e) acc[e] += wt * __uint_as_float(v[k][e]);
     }
     M = Mg;
   }
@@ -948,11 +965,11 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   const int b = unit / p.Hkv, kvh = unit - b * p.Hkv;
   const uint32_t u = uint32_t(row) / uint32_t(p.group);
   const int h = kvh * p.group + (row - int(u) * p.group);
-  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kD + 8 * d8;
-  bf16x8 ov;
+  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kD + 4 * d4;
+  bf16x4 ov;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ov[e] = static_cast<bf16>(acc[e] * inv);
-  *reinterpret_cast<bf16x8*>(o) = ov;
+  for (int e = 0; e < 4; ++e) ov[e] = static_cast<bf16>(acc[e] * inv);
+  *reinterpret_cast<bf16x4*>(o) = ov;
 }
 
 }  // namespace
@@ -988,7 +1005,7 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   if (st != MEDUSA_OK) return st;
   MergeArgs m{};
   m.ml = static_cast<const float2*>(a.workspace);
-  m.o = reinterpret_cast<const bf16*>(static_cast<const unsigned char*>(a.workspace) + plan.o_offset);
+  m.o = reinterpret_cast<const float*>(static_cast<const unsigned char*>(a.workspace) + plan.o_offset);
   m.out = a.out;
   m.status = a.status;
   m.Hq = a.Hq;
@@ -1000,7 +1017,7 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   m.qblocks = plan.qblocks;
   m.splits = plan.splits;
   return launch(reinterpret_cast<const void*>(&tree_attn_merge_kernel),
-                dim3(unsigned(plan.units), unsigned(plan.qblocks), unsigned((plan.qrows + 15) / 16)),
+                dim3(unsigned(plan.units), unsigned(plan.qblocks), unsigned((plan.qrows + kMergeRows - 1) / kMergeRows)),
                 dim3(256), 0, stream, m, nullptr, ev_stop);
 }
 

@@ -12,16 +12,17 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from gpu_support import TOL, AttnRun, announce, compile_both, host, sample_rows  # noqa: E402
+from gpu_support import TOL, AttnRun, announce, compile_both, host  # noqa: E402
 
 
 def _all_rows(w, N):
     return [(b, u, h) for b in range(w.B) for u in range(N) for h in range(w.Hq)]
 
 
-@pytest.mark.parametrize("name,n_rows", [("tiny", None), ("llama7b", None), ("gqa8b", 192),
-                                         ("wide", 192), ("batched", 256)])
-def test_workload_attention(name, n_rows):
+@pytest.mark.parametrize("name", ["tiny", "llama7b", "gqa8b", "wide", "batched"])
+def test_workload_attention(name):
+    """Every output row of every workload, in the launch configuration the benchmark
+    times, against the binary64 per-path oracle."""
     w = workloads.WORKLOADS[name]
     announce(f"attention workload={name}")
     lib, ora = compile_both(w)
@@ -29,14 +30,10 @@ def test_workload_attention(name, n_rows):
     N = x["N"]
     run = AttnRun(w, x, lib, ora)
     assert run.run() == 0
-    if n_rows is None:
-        rows = _all_rows(w, N)
-    else:
-        # always include the root, the deepest rows, first and last heads, every sequence
-        must = [(b, u, h) for b in range(w.B) for u in (0, N - 1) for h in (0, w.Hq - 1)]
-        rows = sample_rows(w, N, n_rows, seed=1, must=must)
+    rows = _all_rows(w, N)
+    announce(f"  oracle over all {len(rows)} rows")
     err, staged = run.check(rows)
-    announce(f"  max abs err {err:.3e}, staged-row error {staged:.3f} ulp-bound")
+    announce(f"  max abs err {err:.3e}, staged-row error {staged:.3f} of its bound")
     assert err <= TOL[w.dtype]
     assert staged <= 1.0
 
@@ -131,32 +128,30 @@ def test_repeated_calls_reuse_the_workspace():
     assert torch.equal(first, run.out)
 
 
-def test_running_maximum_moves_inside_the_key_stream():
-    """Committed keys whose scale climbs from 1 to 6 along each quarter of the context (a
-    sawtooth): the largest score of a key range grows by far more than the 2^8 slack (about
-    3 to 26 in log2 units), so the running maximum moves, with O and l rescaled, in the
-    middle of every workgroup's key stream.  A tile mishandled around a move is off by a
-    factor of at least 2^8 and shows as an error of order |v|.
+@pytest.mark.parametrize("amp", [6, 16])
+def test_running_maximum_moves_inside_the_key_stream(amp):
+    """Committed keys whose scale climbs from 1 to `amp` along each quarter of the context (a
+    sawtooth), values at unit scale: the largest score of a key range grows by far more than
+    the 2^8 slack (about 3 to 70 in log2 units), so the running maximum moves, with O and l
+    rescaled, in the middle of every workgroup's key stream, and the softmax is peaked.  A
+    tile mishandled around a move is off by a factor of at least 2^8 and shows as an error
+    of order |v|.
 
-    Precision: the rotated queries are rounded to bf16 (relative 2^-9) for the matrix
-    core, so a score near 20 carries an absolute error near 0.04, and a peaked softmax
-    passes that on to the output instead of averaging it out.  The values are drawn at a
-    quarter of the unit scale, which keeps that effect (about 5e-3 here) inside the bf16
-    tolerance."""
+    Precision: a score is q~ . k with |q~||k| up to about 16 sqrt(d_h) here.  The kernel
+    carries q~ as a hi/lo pair of bf16 operands (exact to about 2^-17), so the score error is
+    far below what a peaked softmax would pass on; what remains is the bf16 rounding of the
+    output (half an ulp, 2^-9 of |o| up to 2^-8) and of the probabilities.  Every row is
+    compared."""
     w = dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=8, Hkv=2)
-    announce("attention with a climbing score scale (running-maximum moves)")
+    announce(f"attention with a climbing score scale to {amp} (running-maximum moves), unit-scale V")
     lib, ora = compile_both(w)
     x = workloads.draw_round(w, seed=31, prefix_len=[4096, 3001])
-    scale = 1.0 + 5.0 * (np.arange(x["S_max"]) % 1024) / 1024
+    scale = 1.0 + (amp - 1.0) * (np.arange(x["S_max"]) % 1024) / 1024
     x["k_cache"] = workloads.round_to_dtype(
         x["k_cache"] * scale[None, None, :, None].astype(np.float32), w.dtype)
-    x["v_cache"] = workloads.round_to_dtype(x["v_cache"] * np.float32(0.25), w.dtype)
-    x["v_new"] = workloads.round_to_dtype(x["v_new"] * np.float32(0.25), w.dtype)
     run = AttnRun(w, x, lib, ora)
     assert run.run() == 0
-    N = x["N"]
-    must = [(b, u, h) for b in range(w.B) for u in (0, N - 1) for h in (0, w.Hq - 1)]
-    err, staged = run.check(sample_rows(w, N, 96, seed=2, must=must))
+    err, staged = run.check(_all_rows(w, x["N"]))
     announce(f"  max abs err {err:.3e}")
     assert err <= TOL[w.dtype] and staged <= 1.0
 
@@ -191,7 +186,7 @@ def test_deepest_supported_chain_and_the_first_unsupported_depth():
 def test_batch_of_more_than_64_sequences():
     """70 sequences on the matrix-core path: the prefix lengths are checked 64 per pass, so a
     sequence past the first 64 that does not fit must fail the round (no stores), and a
-    fitting batch must match the oracle on rows of sequences on both sides of 64."""
+    fitting batch must match the oracle on every row of every sequence."""
     w = dataclasses.replace(workloads.WORKLOADS["batched"], B=70, Hq=4, Hkv=1, tree="cartesian",
                             branching=(2, 2), num_heads=2, topk=2, slack=3)
     announce("attention with 70 sequences")
@@ -202,8 +197,7 @@ def test_batch_of_more_than_64_sequences():
     run = AttnRun(w, x, lib, ora)
     assert run.run() == 0
     N = x["N"]
-    must = [(b, u, h) for b in (0, 63, 64, 69) for u in (0, N - 1) for h in (0, w.Hq - 1)]
-    err, staged = run.check(sample_rows(w, N, 64, seed=3, must=must))
+    err, staged = run.check(_all_rows(w, N))
     announce(f"  max abs err {err:.3e}")
     assert err <= TOL[w.dtype] and staged <= 1.0
 
