@@ -205,6 +205,33 @@ medusa_status medusa_tree_attn(void* stream, medusa_dtype dt, int32_t B, int32_t
                                size_t workspace_bytes, int32_t* d_status, void* ev_start,
                                void* ev_stop);
 
+/* ------------------------------------------------------------------ tree attention, no allocation
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Computes exactly what
+ * medusa_tree_attn computes, with the same arguments except the workspace; the split
+ * partials go to a device array of MEDUSA_TREE_ATTN_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends (its address is taken on the first
+ * call made with that GPU current; that call and no later one may load the library's code
+ * object on the device).  No call allocates or frees memory.
+ * The array is shared by every call on one GPU: calls that overlap on one GPU (different
+ * streams, no ordering between them) race and their outputs are undefined; calls on one
+ * stream are ordered and independent.
+ * Limit: a shape whose workspace (medusa_tree_attn_workspace_size) exceeds the array gets
+ * MEDUSA_ECAPACITY before any launch; every shape medusa_tree_attn supports fits.
+ * Errors: those of medusa_tree_attn, plus MEDUSA_EHIP if the array's address cannot be
+ * taken on the current GPU.
+ */
+#define MEDUSA_TREE_ATTN_SCRATCH_BYTES ((size_t)256 * 128 * (8 + 128 * 4))
+
+medusa_status medusa_tree_attn_noalloc(void* stream, medusa_dtype dt, int32_t B, int32_t Hq, int32_t Hkv,
+                                       int32_t d_h, int32_t N, const int32_t* d_depth,
+                                       const uint64_t* d_tree_mask, int32_t mask_words,
+                                       const int32_t* d_prefix_len, const void* q, const void* k_new,
+                                       const void* v_new, void* k_cache, void* v_cache, int32_t S_max,
+                                       double rope_base, void* out, int32_t* d_status, void* ev_start,
+                                       void* ev_stop);
+
 /* ------------------------------------------------------------------ acceptance
  *
  * [M7.2] §0x03D and §0x04D; [PartII] Part 7.  Per sequence b:

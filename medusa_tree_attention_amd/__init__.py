@@ -4,6 +4,7 @@ The four calls of one verification round, with the names of the C entry points:
 
     medusa_tree_compile   host tree compiler
     medusa_tree_attn      HIP tree attention (RoPE at P + depth, staged K/V rows)
+    medusa_tree_attn_noalloc  the same with the library's own partials array
     medusa_accept         HIP greedy acceptance
     medusa_accept_typical HIP fast typical acceptance
     medusa_kv_compact     HIP winning-path K/V compaction
@@ -14,5 +15,5 @@ from ._binding import (  # noqa: F401
     medusa_accept_typical,
     medusa_accept_workspace_size, medusa_head_candidates, medusa_head_workspace_size,
     medusa_kv_compact, medusa_read_probe, medusa_read_probe_sink_size, medusa_tree_attn,
-    medusa_tree_attn_workspace_size, medusa_tree_budget, medusa_tree_compile,
+    medusa_tree_attn_noalloc, medusa_tree_attn_workspace_size, medusa_tree_budget, medusa_tree_compile,
 )

@@ -54,6 +54,8 @@ _SIGNATURES = {
     "medusa_tree_attn_workspace_size": (_SZ, [_I32] * 7),
     "medusa_tree_attn": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _P, _P,
                                 _P, _P, _P, _I32, _D, _P, _P, _SZ, _P, _P, _P]),
+    "medusa_tree_attn_noalloc": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _P, _P,
+                                        _P, _P, _P, _I32, _D, _P, _P, _P, _P]),
     "medusa_accept_workspace_size": (_SZ, [_I32, _I32]),
     "medusa_accept": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P,
                              _P, _P, _P, _SZ, _P, _P, _P]),
@@ -201,6 +203,18 @@ def medusa_tree_attn(q, k_new, v_new, k_cache, v_cache, depth, tree_mask, prefix
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _ptr(status), ev_start, ev_stop)
     _check("medusa_tree_attn", code)
+
+
+def medusa_tree_attn_noalloc(q, k_new, v_new, k_cache, v_cache, depth, tree_mask, prefix_len, rope_base,
+                             out, status, stream=None, ev_start=None, ev_stop=None):
+    """medusa_tree_attn with the split partials in the library's own device array."""
+    B, N, Hq, d = q.shape
+    Hkv, S_max = k_new.shape[2], k_cache.shape[2]
+    code = load().medusa_tree_attn_noalloc(
+        _stream(stream), _dtype_code(q), B, Hq, Hkv, d, N, _ptr(depth), _ptr(tree_mask),
+        tree_mask.shape[1], _ptr(prefix_len), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+        _ptr(v_cache), S_max, float(rope_base), _ptr(out), _ptr(status), ev_start, ev_stop)
+    _check("medusa_tree_attn_noalloc", code)
 
 
 # ------------------------------------------------------------------ acceptance

@@ -13,7 +13,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmedusa.so")
 INCLUDE = os.path.join(ROOT, "include")
 
-HIP_SOURCES = ["attn.hip", "attn_mfma.hip", "accept.hip", "compact.hip", "heads.hip", "probe.hip"]
+HIP_SOURCES = ["attn.hip", "attn_mfma.hip", "attn_noalloc.hip", "accept.hip", "compact.hip", "heads.hip",
+               "probe.hip"]
 CPP_SOURCES = ["tree_compile.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -40,6 +40,10 @@ __device__ __forceinline__ bool prefixes_fit(const AttnArgs& a) {
   return __ballot(bad) == 0;
 }
 
+// The largest workspace the attention call asks for.  Split partials exist only when the
+// grid has at most 256 workgroups; each holds 128 query rows of (m, l) and 128 fp32 values.
+constexpr size_t kAttnWorkspaceMax = size_t(256) * 128 * (8 + 128 * 4);
+
 // Host-side dispatch helpers implemented next to the MFMA kernel.
 bool mfma_path_applies(medusa_dtype dt, int32_t Hq, int32_t Hkv, int32_t d_h, int32_t N);
 size_t attn_workspace_bytes(medusa_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d_h,

@@ -116,6 +116,10 @@ struct Plan {
   size_t o_offset, bytes;
 };
 
+static_assert(size_t(kTargetWGs) * (kRowsWave * kWaves / kKeyPhases) * (sizeof(float2) + kD * sizeof(float)) <=
+                  kAttnWorkspaceMax,
+              "the split partials of the largest plan fit the stated workspace bound");
+
 Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
   Plan p{};
   p.units = B * Hkv;
