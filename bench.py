@@ -191,11 +191,29 @@ def read_ceiling_gbs(torch, M):
     return 2 ** 30 / sec / 1e9
 
 
-def cpu_baseline(w, x, xh=None):
-    """The CPU oracle, as it stands, on the same round: every sequence, head and node (and,
-    given the head inputs ``xh``, the head step that fills the candidates first)."""
-    import numpy as np
+# The CPU oracle runs in a child process started before this process makes any HIP call (a
+# process that has initialised the GPU is never forked or replaced); the child spreads the
+# per-path attention over a pool of forked workers, one BLAS thread each.
+_CPU_CTX = {}
+
+
+def _oracle_rows(rows):
+    """Worker: the oracle's attention outputs for a chunk of (b, u, h) rows."""
     from threadpoolctl import threadpool_limits
+
+    from oracle import attention as A
+    x, ora, base = _CPU_CTX["x"], _CPU_CTX["ora"], _CPU_CTX["rope_base"]
+    with threadpool_limits(limits=1):
+        out, _, _ = A.tree_attention(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                                     x["prefix_len"], ora["depth"], ora["parent"], base, rows=rows)
+    return [(r, out[r]) for r in rows]
+
+
+def _oracle_round(w, x, xh, pool, n_chunks):
+    """One round through the oracle: the head step (given its inputs), tree compile, every
+    row's per-path attention (over the pool, or in this process), greedy acceptance and
+    the compaction of the staged rows."""
+    import numpy as np
 
     import workloads
     from oracle import accept as AC
@@ -205,28 +223,88 @@ def cpu_baseline(w, x, xh=None):
     from oracle import tree as T
 
     spec = workloads.tree_spec(w)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        cand = x["candidates"]
-        if xh is not None:
-            cand = HD.head_candidates(xh["h"], xh["W1"], xh["W2"], xh["root_tokens"], w.topk)["candidates"]
-        ora = (T.compile_tree(spec["paths"], w.num_heads, w.topk) if spec["paths"] is not None
-               else T.compile_greedy(spec["rank_hit"], spec["n_nodes"]))
+    cand = x["candidates"]
+    if xh is not None:
+        cand = HD.head_candidates(xh["h"], xh["W1"], xh["W2"], xh["root_tokens"], w.topk)["candidates"]
+    ora = (T.compile_tree(spec["paths"], w.num_heads, w.topk) if spec["paths"] is not None
+           else T.compile_greedy(spec["rank_hit"], spec["n_nodes"]))
+    rows = [(b, u, h) for b in range(w.B) for u in range(x["N"]) for h in range(w.Hq)]
+    if pool is None:
         _, sk, sv = A.tree_attention(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
                                      x["prefix_len"], ora["depth"], ora["parent"], w.rope_base)
-        res = AC.accept_batch(ora, cand, logits=x["logits"], target_ids=x["target_ids"])
-        cache = [np.array(x["k_cache"], np.float64), np.array(x["v_cache"], np.float64)]
-        for b in range(w.B):
-            P = int(x["prefix_len"][b])
-            for c, st in zip(cache, (sk, sv)):
-                c[b, :, P:P + x["N"]] = st[b]
-        C.kv_compact(cache, ora["retrieve"], res["best_path"], res["accept_len"], x["prefix_len"], x["N"])
-        dt = time.perf_counter() - t0
-    return {"value": w.B * x["N"] / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
-            "sample": (f"one full round of the workload ({w.B} sequences x {x['N']} nodes x {w.Hq} heads "
-                       f"at P={w.P}): " + ("binary64 head step (4 heads, top-k), " if xh is not None else "")
-                       + f"tree compile, per-path binary64 attention, greedy accept, "
-                       f"compaction; {dt:.1f} s on 1 thread of {cpu_model()}")}
+    else:
+        # the workers were forked with the inputs and this same tree in _CPU_CTX
+        chunks = [rows[i::n_chunks] for i in range(n_chunks)]
+        out = np.full((w.B, x["N"], w.Hq, w.d), np.nan)
+        for part in pool.map(_oracle_rows, chunks):
+            for r, v in part:
+                out[r] = v
+        # the staged K/V rows (no attention rows) for the compaction
+        _, sk, sv = A.tree_attention(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                                     x["prefix_len"], ora["depth"], ora["parent"], w.rope_base, rows=[])
+    res = AC.accept_batch(ora, cand, logits=x["logits"], target_ids=x["target_ids"])
+    cache = [np.array(x["k_cache"], np.float64), np.array(x["v_cache"], np.float64)]
+    for b in range(w.B):
+        P = int(x["prefix_len"][b])
+        for c, st in zip(cache, (sk, sv)):
+            c[b, :, P:P + x["N"]] = st[b]
+    C.kv_compact(cache, ora["retrieve"], res["best_path"], res["accept_len"], x["prefix_len"], x["N"])
+
+
+def cpu_baseline_child(w, full_round):
+    """The CPU oracle, as it stands, on one full round of the workload: on every core this
+    process may use (a pool of forked workers, capped at 16, the machine's CPU share per GPU),
+    and on one thread."""
+    import multiprocessing
+
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import workloads
+    x = workloads.draw_round(w)
+    xh = workloads.draw_heads(w.seed + 300, w.B, w.num_heads, w.Hq * w.d, w.vocab) if full_round else None
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, 16))
+    from oracle import tree as T
+    spec = workloads.tree_spec(w)
+    _CPU_CTX.update(x=x, rope_base=w.rope_base,
+                    ora=(T.compile_tree(spec["paths"], w.num_heads, w.topk) if spec["paths"] is not None
+                         else T.compile_greedy(spec["rank_hit"], spec["n_nodes"])))
+    with multiprocessing.get_context("fork").Pool(workers) as pool:
+        pool.map(abs, range(workers))  # workers started before the timed region
+        with threadpool_limits(limits=workers):  # the head step's matrix products in this process
+            t0 = time.perf_counter()
+            _oracle_round(w, x, xh, pool, 4 * workers)
+            dt_all = time.perf_counter() - t0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        _oracle_round(w, x, xh, None, 1)
+        dt_one = time.perf_counter() - t0
+    blas = sorted({i.get("internal_api", "?") + ":" + str(i.get("num_threads")) for i in threadpool_info()})
+    nodes = w.B * x["N"]
+    return {"value": nodes / dt_all, "unit": "nodes/s", "cores": workers, "kind": "oracle",
+            "affinity_cores": affinity, "blas_threads_per_worker": 1, "blas": blas,
+            "cpu_model": cpu_model(), "seconds": dt_all,
+            "single_thread": {"value": nodes / dt_one, "seconds": dt_one},
+            "sample": (f"one full round of the workload ({w.B} sequences x {x['N']} nodes x {w.Hq} heads at "
+                       f"P={w.P}): " + ("binary64 head step (4 heads, top-k), " if full_round else "")
+                       + f"tree compile, per-path binary64 attention of every row over {workers} forked "
+                       f"workers (one BLAS thread each), greedy accept, compaction; {dt_all:.2f} s "
+                       f"({dt_one:.1f} s on one thread) on {cpu_model()}")}
+
+
+def run_cpu_baseline(args):
+    """Start the oracle baseline as a child process (before any HIP call here) and return its
+    JSON record, or None if it failed."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", args.workload,
+           "--prefix", str(args.prefix), "--round", args.round]
+    log("[bench] timing the CPU oracle on one round (child process) ...")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    if r.returncode != 0 or not lines:
+        log(f"[bench] CPU baseline failed ({r.returncode}): {r.stderr[-500:]}")
+        return None
+    return json.loads(lines[-1])
 
 
 def budget_sweep(args, np, torch, M, workloads):
@@ -332,7 +410,17 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_baseline_child:  # the oracle baseline in a process that never touches the GPU
+        import dataclasses
+
+        import workloads
+        w = workloads.WORKLOADS[args.workload]
+        if args.prefix:
+            w = dataclasses.replace(w, P=args.prefix)
+        print(json.dumps(cpu_baseline_child(w, args.round == "full")), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the round is measured per GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
@@ -352,6 +440,8 @@ def main():
         import dataclasses
         w = dataclasses.replace(w, P=args.prefix)
     spec = workloads.tree_spec(w)
+    # the CPU oracle first, in a child process, before this process makes any HIP call
+    cpu_record = None if args.no_cpu else run_cpu_baseline(args)
     M.load()  # the library's first load is not part of the compile time
     t0 = time.perf_counter()
     tree = (M.medusa_tree_compile(w.num_heads, w.topk, paths=spec["paths"]) if spec["paths"] is not None
@@ -449,15 +539,16 @@ def main():
     ev = HipEvents()
     events = [(ev.create(), ev.create()) for _ in range(total)]
     head_events = [(ev.create(), ev.create()) for _ in range(total)] if heads is not None else []
+    acc_events = [(ev.create(), ev.create()) for _ in range(total)]
     no_events = (None, None)
 
-    def step(call, evs, hevs):
+    def step(call, evs, hevs, aevs=no_events):
         attn, acc, cmp_, head = call
         rc = 0
         if head is not None:
             rc |= lib.medusa_head_candidates(*head, *hevs)
         rc |= lib.medusa_tree_attn(*attn, *evs)
-        rc |= accept_fn(*acc, None, None)
+        rc |= accept_fn(*acc, *aevs)
         if cmp_ is not None:
             rc |= lib.medusa_kv_compact(*cmp_, None, None)
         if rc:
@@ -467,11 +558,11 @@ def main():
     calls = build_calls(sptr, ctl, total)
     hev = lambda i: head_events[i] if head_events else no_events
     for i in range(args.warmup):
-        step(calls[i], events[i], hev(i))
+        step(calls[i], events[i], hev(i), acc_events[i])
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.warmup, total):
-        step(calls[i], events[i], hev(i))
+        step(calls[i], events[i], hev(i))  # acceptance timed by events in the warm-up steps only
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
 
@@ -503,7 +594,12 @@ def main():
         raise RuntimeError(f"device status words {sorted(set(statuses.tolist()))}: the round failed")
     attn_ms = np.array([ev.elapsed_ms(a, b) for a, b in events[args.warmup:]])
     head_ms = np.array([ev.elapsed_ms(a, b) for a, b in head_events[args.warmup:]])
-    for a, b in events + head_events:
+    # the acceptance call's events add host launch cost, so they are recorded in the untimed
+    # warm-up steps only
+    acc_ms = np.array([ev.elapsed_ms(a, b) for a, b in acc_events[:args.warmup]] or [float("nan")])
+    # tokens each timed step committed per sequence: the compaction advanced P_b by G_b
+    committed = ctl[args.warmup:, :w.B].cpu().numpy().astype(np.int64) - x["prefix_len"][None, :].astype(np.int64)
+    for a, b in events + head_events + acc_events:
         ev.destroy(a)
         ev.destroy(b)
 
@@ -545,6 +641,20 @@ def main():
                      "read_ceiling_gbs": ceiling_gbs, "frac_of_read_ceiling": achieved / ceiling_gbs},
         "attention_nodes_per_s": w.B * N / mean_s,
         "tree_compile_us": compile_us,
+        # what [Chai]'s engineering notes ask a round to record: the tree's shape, the
+        # committed-token distribution G, and per-stage latency
+        "round_metrics": {
+            "nodes": N, "nodes_per_depth": np.bincount(tree["depth"]).tolist(),
+            "n_paths": tree["n_paths"], "path_width": tree["path_width"],
+            "committed_tokens_G": {
+                "mean": float(committed.mean()),
+                "per_sequence_mean": committed.mean(axis=0).tolist(),
+                "histogram": {str(int(g)): int(c) for g, c in zip(*np.unique(committed, return_counts=True))}},
+            "stage_us": {"attention": float(attn_ms.mean()) * 1e3,
+                         "accept" + ("_commit" if fused else ""): float(acc_ms.mean()) * 1e3,
+                         **({"head": float(head_ms.mean()) * 1e3} if heads is not None else {}),
+                         "round_step": elapsed / args.steps * 1e6},
+        },
     }
     if w.dtype == "bf16":  # the matrix-core path; its peak is the dense bf16 MFMA rate
         flops = algorithmic_flops(w, N)
@@ -576,9 +686,8 @@ def main():
     log(f"[bench] attention mean {mean_s * 1e6:.2f} us -> {achieved:.0f} GB/s "
         f"({achieved / HBM_PEAK_GBS:.1%} of HBM peak, {achieved / ceiling_gbs:.1%} of the "
         f"{ceiling_gbs:.0f} GB/s read ceiling); step {elapsed / args.steps * 1e6:.1f} us")
-    if not args.no_cpu:
-        log("[bench] timing the CPU oracle on one round ...")
-        result["cpu_baseline"] = cpu_baseline(w, x, xh)
+    if cpu_record is not None:
+        result["cpu_baseline"] = cpu_record
     print(json.dumps(result), flush=True)
 
 

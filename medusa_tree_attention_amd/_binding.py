@@ -100,6 +100,29 @@ def _check(fn, code):
         raise MedusaError(fn, code)
 
 
+VALIDATE_ENV = "MEDUSA_VALIDATE"
+
+
+def validating():
+    """True when MEDUSA_VALIDATE is set to a non-empty value other than 0: every device entry
+    point then waits for its work and checks the round's status word (a debugging mode; the
+    library itself never synchronises)."""
+    return os.environ.get(VALIDATE_ENV, "0") not in ("", "0")
+
+
+def _validate(fn, status):
+    """In validation mode: synchronise the status word's device and raise MedusaError if
+    the word holds an error code."""
+    if not validating():
+        return
+    if getattr(status, "is_cuda", False):
+        import torch
+        torch.cuda.synchronize(status.device)
+    code = int(status.reshape(-1)[0].item())
+    if code != 0:
+        raise MedusaError(fn + " (device status word)", code)
+
+
 def _ptr(t):
     """Device pointer of a torch tensor (or None)."""
     if t is None:
@@ -203,6 +226,7 @@ def medusa_tree_attn(q, k_new, v_new, k_cache, v_cache, depth, tree_mask, prefix
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _ptr(status), ev_start, ev_stop)
     _check("medusa_tree_attn", code)
+    _validate("medusa_tree_attn", status)
 
 
 def medusa_tree_attn_noalloc(q, k_new, v_new, k_cache, v_cache, depth, tree_mask, prefix_len, rope_base,
@@ -215,6 +239,7 @@ def medusa_tree_attn_noalloc(q, k_new, v_new, k_cache, v_cache, depth, tree_mask
         tree_mask.shape[1], _ptr(prefix_len), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
         _ptr(v_cache), S_max, float(rope_base), _ptr(out), _ptr(status), ev_start, ev_stop)
     _check("medusa_tree_attn_noalloc", code)
+    _validate("medusa_tree_attn_noalloc", status)
 
 
 # ------------------------------------------------------------------ acceptance
@@ -237,6 +262,7 @@ def medusa_accept(candidates, tree_indices, retrieve, best_path, accept_len, acc
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _ptr(status), ev_start, ev_stop)
     _check("medusa_accept", code)
+    _validate("medusa_accept", status)
 
 
 def medusa_accept_typical(candidates, tree_indices, retrieve, best_path, accept_len, accepted_tokens,
@@ -253,6 +279,7 @@ def medusa_accept_typical(candidates, tree_indices, retrieve, best_path, accept_
         _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _ptr(status), ev_start, ev_stop)
     _check("medusa_accept_typical", code)
+    _validate("medusa_accept_typical", status)
 
 
 def medusa_accept_commit(candidates, tree_indices, retrieve, best_path, accept_len, accepted_tokens,
@@ -280,6 +307,7 @@ def medusa_accept_commit(candidates, tree_indices, retrieve, best_path, accept_l
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _ptr(status), ev_start, ev_stop)
     _check("medusa_accept_commit", code)
+    _validate("medusa_accept_commit", status)
 
 
 # ------------------------------------------------------------------ head step
@@ -298,6 +326,7 @@ def medusa_head_candidates(h, W1, W2, root_tokens, candidates, status, workspace
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _ptr(status), ev_start, ev_stop)
     _check("medusa_head_candidates", code)
+    _validate("medusa_head_candidates", status)
 
 
 # ------------------------------------------------------------------ compaction
@@ -316,6 +345,7 @@ def medusa_kv_compact(k_caches, v_caches, retrieve, best_path, accept_len, prefi
         n_paths, width, _ptr(best_path), _ptr(accept_len), _ptr(prefix_len), _ptr(status),
         ev_start, ev_stop)
     _check("medusa_kv_compact", code)
+    _validate("medusa_kv_compact", status)
 
 
 # ------------------------------------------------------------------ measurement utility

@@ -67,5 +67,26 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+HOST_SANITIZED = os.path.join(BUILD, "libmedusa_host_sanitized.so")
+
+
+def build_host_sanitized(verbose: bool = True) -> str:
+    """The host C++ (tree compile and node budget) alone, built with AddressSanitizer and
+    UndefinedBehaviorSanitizer into a CPU-only library for the host tests.  It is loaded
+    with the ASan runtime preloaded; it exports only the host entry points."""
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = HOST_SANITIZED + ".tmp"
+    _run([["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-ffp-contract=off",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-I", INCLUDE, *[os.path.join(CSRC, src) for src in CPP_SOURCES], "-o", tmp]])
+    shutil.move(tmp, HOST_SANITIZED)
+    if verbose:
+        print(f"[build] wrote {HOST_SANITIZED}", flush=True)
+    return HOST_SANITIZED
+
+
 if __name__ == "__main__":
-    build()
+    if sys.argv[1:] == ["host-sanitized"]:
+        build_host_sanitized()
+    else:
+        build()

@@ -74,6 +74,7 @@ constexpr int kRowsWave = 32;    // query rows per wavefront
 constexpr int kRing = 8;         // tile buffers in LDS
 constexpr int kTileBytes = 2 * kTile * kD * 2;  // K then V of one tile
 constexpr int kTableDepth = 32;  // RoPE phases kept in LDS; deeper trees are rejected
+constexpr int kEarlyDepth = 8;   // phases formed before the node depths are known
 constexpr int kDepthLds = 4096;  // node depths cached in LDS (bytes); later nodes read memory
 constexpr int kMaskLds = 8;      // staged tiles whose visibility words are kept in LDS
 constexpr int kTargetWGs = 256;  // one workgroup per compute unit
@@ -401,21 +402,22 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   if (ring_ok) issue_stage(0);
   const int n_ring_loads = ring_ok ? 2 * kDmaOps * (tile_end(0) - tile_start(0)) : 0;
 
-  // ---- RoPE phases (cos, sin) of positions P + d for every depth d < 32: the angle is
-  // formed and reduced modulo 2 pi in binary64, then evaluated in fp32.  Thread tid fills
-  // entries (d, tid % 64) for d = tid / 64 + 8 k.  This needs only P, so it runs while
-  // the set-up loads and the first stage's tiles are in flight.
-  static_assert(kThreads % (kD / 2) == 0, "a thread's phase entries share one frequency");
+  // ---- RoPE phases (cos, sin) of positions P + d: the angle is formed and reduced modulo
+  // 2 pi in binary64, then evaluated in fp32.  The depths below kEarlyDepth need only P and
+  // are formed while the set-up loads and the first stage's tiles are in flight, one entry
+  // per thread: (d, tid % 64) with d = tid / 64.  Deeper phases, which few trees need, are
+  // formed once the node depths are known.
+  static_assert(kThreads == kEarlyDepth * (kD / 2), "one early phase entry per thread");
   const double theta = exp2(-double(tid % (kD / 2)) * (2.0 / kD) * p.log2_base);
-  for (int i = tid; i < kTableDepth * (kD / 2); i += kThreads) {
-    const int d = i / (kD / 2), j = i % (kD / 2);
+  auto phase = [&](int d) __attribute__((always_inline)) {
     const double x = double(P + d) * theta;
     const double k = rint(x * kInvTwoPi);
     const float r = float(fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, x)));
     float sn, cs;
     sincosf(r, &sn, &cs);
-    s_cs[d][j] = make_float2(cs, sn);
-  }
+    s_cs[d][tid % (kD / 2)] = make_float2(cs, sn);
+  };
+  phase(tid / (kD / 2));
   // the set-up loads are older than the ring's tile loads, which may stay in flight
   wait_vm(n_ring_loads);
   pin(st_word);
@@ -453,23 +455,31 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     for (int s = 0; s < 8; ++s) raw[s] = u32x4{0u, 0u, 0u, 0u};
   }
   bool bad = tid < N && (dep0 < 0 || dep0 >= kTableDepth);
+  bool deep = tid < N && dep0 >= kEarlyDepth;
   if (tid < N && tid < kDepthLds) s_dep[tid] = static_cast<unsigned char>(dep0);
   for (int i = tid + kThreads; i < N; i += kThreads) {  // trees of more than 512 nodes
     const int d = a.depth[i];
     bad = bad || d < 0 || d >= kTableDepth;
+    deep = deep || d >= kEarlyDepth;
     if (i < kDepthLds) s_dep[i] = static_cast<unsigned char>(d);
   }
 
-  if (lane == 0) s_bad[wave] = 0;
-  if (__ballot(bad) != 0 && lane == 0) s_bad[wave] = 1;
+  // one flag word per wavefront (every lane votes): bit 0 a depth outside the table, bit 1
+  // a depth beyond the phases formed so far
+  const int wflags = (__ballot(bad) != 0 ? 1 : 0) | (__ballot(deep) != 0 ? 2 : 0);
+  if (lane == 0) s_bad[wave] = wflags;
   __syncthreads();
-  int any_bad = 0;
+  int flags = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) any_bad |= s_bad[w];
-  if (any_bad) {  // a node deeper than the phase table: uniform over the workgroup
-    wait_vm(0);   // no load may still target LDS when the block exits
+  for (int w = 0; w < kWaves; ++w) flags |= s_bad[w];
+  if (flags & 1) {  // a node deeper than the phase table: uniform over the workgroup
+    wait_vm(0);     // no load may still target LDS when the block exits
     if (blockIdx.x == 0 && tid == 0) raise_status(a.status, MEDUSA_EUNSUPPORTED);
     return;
+  }
+  if (flags & 2) {  // deep trees: the remaining phases
+    for (int d = kEarlyDepth + tid / (kD / 2); d < kTableDepth; d += kThreads / (kD / 2)) phase(d);
+    __syncthreads();
   }
 
   // ---- this wavefront's 32 query rows: rotated, scaled to log2 units, bf16 B operands;
