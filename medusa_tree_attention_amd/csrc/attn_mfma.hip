@@ -918,59 +918,61 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     }
 }
 
-// Merge of the splits: thread (row, 4 dims) combines the splits' partials, weighting split
-// s by l_s 2^(m_s - M).  The splits are visited eight at a time with every load of a group
-// issued before any is used, so that a thread waits for memory once per group rather than
-// once per split.
-constexpr int kMergeGroup = 8;
-constexpr int kMergeRows = 8;  // query rows per 256-thread block
+// Merge of the splits: thread (row, 8 dims) combines the splits' partials, weighting split
+// s by l_s 2^(m_s - M).  The splits are visited kGroup at a time (four when there are at
+// most four, else eight) with every load of a group issued before any is used, so that a
+// thread waits for memory once per group rather than once per split.
+constexpr int kMergeRows = 16;  // query rows per 256-thread block: 16 threads per row
 
-// Grid: x = unit, y = query block, z = 8-row chunk of the query block, so that every index
+// Grid: x = unit, y = query block, z = 16-row chunk of the query block, so that every index
 // comes from the launch coordinates without a division by a run-time value.
+template <int kGroup>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   const bool failed = round_failed(p.status);  // gates the store only
-  const int d4 = threadIdx.x & 31;
-  const int r = int(blockIdx.z) * kMergeRows + (threadIdx.x >> 5);  // row of the query block
+  const int d8 = threadIdx.x & 15;
+  const int r = int(blockIdx.z) * kMergeRows + (threadIdx.x >> 4);  // row of the query block
   const int qb = int(blockIdx.y), unit = int(blockIdx.x);
   const int row = qb * p.qrows + r;
   if (r >= p.qrows || row >= p.rows) return;
   const int64_t base = (int64_t(unit) * p.qblocks + qb) * p.splits * p.qrows + r;  // slot of split 0
   float M = -INFINITY, L = 0.f;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < p.splits; s0 += kMergeGroup) {
-    // issued as inline assembly, all sixteen loads back to back and then one wait: left to
-    // itself the compiler waits for each split's load before it issues the next
-    u32x2 mlw[kMergeGroup];
-    u32x4 v[kMergeGroup];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < p.splits; s0 += kGroup) {
+    // issued as inline assembly, every load of the group back to back and then one wait:
+    // left to itself the compiler waits for each split's load before it issues the next
+    u32x2 mlw[kGroup];
+    u32x4 v[kGroup][2];
 #pragma unroll
-    for (int k = 0; k < kMergeGroup; ++k) {  // slots past the last split re-read split 0
+    for (int k = 0; k < kGroup; ++k) {  // slots past the last split re-read split 0
       const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
       mlw[k] = load_b64(p.ml + slot);
-      v[k] = load_b128(p.o + slot * kD + 4 * d4);
+      v[k][0] = load_b128(p.o + slot * kD + 8 * d8);
+      v[k][1] = load_b128(p.o + slot * kD + 8 * d8 + 4);
     }
     wait_vm(0);
-    float2 ml[kMergeGroup];
+    float2 ml[kGroup];
 #pragma unroll
-    for (int k = 0; k < kMergeGroup; ++k) {
+    for (int k = 0; k < kGroup; ++k) {
       pin(mlw[k]);
-      pin(v[k]);
+      pin(v[k][0]);
+      pin(v[k][1]);
       ml[k] = make_float2(__uint_as_float(mlw[k][0]), __uint_as_float(mlw[k][1]));
     }
     float Mg = M;
 #pragma unroll
-    for (int k = 0; k < kMergeGroup; ++k)
+    for (int k = 0; k < kGroup; ++k)
       if (s0 + k < p.splits) Mg = fmaxf(Mg, ml[k].x);
     // rescale what the earlier groups accumulated, then add this group
     const float c = M == -INFINITY ? 0.f : exp2_fast(M - Mg);
     L *= c;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] *= c;
+    for (int e = 0; e < 8; ++e) acc[e] *= c;
 #pragma unroll
-    for (int k = 0; k < kMergeGroup; ++k) {
+    for (int k = 0; k < kGroup; ++k) {
       const float wt = (s0 + k < p.splits && ml[k].x != -INFINITY) ? ml[k].y * exp2_fast(ml[k].x - Mg) : 0.f;
       L += wt;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += wt * __uint_as_float(v[k][e]);
+      for (int e = 0; e < 8; ++e) acc[e] += wt * __uint_as_float(v[k][e >> 2][e & 3]);
     }
     M = Mg;
   }
@@ -979,11 +981,11 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   const int b = unit / p.Hkv, kvh = unit - b * p.Hkv;
   const uint32_t u = uint32_t(row) / uint32_t(p.group);
   const int h = kvh * p.group + (row - int(u) * p.group);
-  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kD + 4 * d4;
-  bf16x4 ov;
+  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kD + 8 * d8;
+  bf16x8 ov;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ov[e] = static_cast<bf16>(acc[e] * inv);
-  *reinterpret_cast<bf16x4*>(o) = ov;
+  for (int e = 0; e < 8; ++e) ov[e] = static_cast<bf16>(acc[e] * inv);
+  *reinterpret_cast<bf16x8*>(o) = ov;
 }
 
 }  // namespace
@@ -1030,8 +1032,9 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   m.qrows = plan.qrows;
   m.qblocks = plan.qblocks;
   m.splits = plan.splits;
-  return launch(reinterpret_cast<const void*>(&tree_attn_merge_kernel),
-                dim3(unsigned(plan.units), unsigned(plan.qblocks), unsigned((plan.qrows + kMergeRows - 1) / kMergeRows)),
+  const void* merge = plan.splits <= 4 ? reinterpret_cast<const void*>(&tree_attn_merge_kernel<4>)
+                                       : reinterpret_cast<const void*>(&tree_attn_merge_kernel<8>);
+  return launch(merge, dim3(unsigned(plan.units), unsigned(plan.qblocks), unsigned((plan.qrows + kMergeRows - 1) / kMergeRows)),
                 dim3(256), 0, stream, m, nullptr, ev_stop);
 }
 
