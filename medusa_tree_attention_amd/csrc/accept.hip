@@ -44,6 +44,10 @@
 
 #include "common.h"
 
+// the device library's wavefront maximum of a float (declared by the HIP headers only under
+// an opt-in macro)
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_max_f32(float);
+
 namespace medusa {
 
 constexpr int kCommitLayers = 32;  // layers one accept-and-commit call compacts
@@ -111,11 +115,29 @@ __device__ __forceinline__ f32x4 load_f32x4(const void* p) {
   asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(v) : "v"(p) : "memory");
   return v;
 }
-// maximum of two floats without the canonicalising moves fmaxf adds
+// maxima without the canonicalising moves fmaxf adds (IEEE: a quiet NaN operand is left out)
 __device__ __forceinline__ float vmax(float x, float y) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
   return r;
+}
+__device__ __forceinline__ float vmax3(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
+// wait until at most n (a constant once unrolled, below 8) of this thread's loads are in flight
+__device__ __forceinline__ void wait_loads(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+  }
 }
 
 constexpr int kArgmaxThreads = 256;
@@ -134,19 +156,16 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(AcceptArgs a) {
   float best = -INFINITY;
   int idx = INT_MAX;
   bool nan = false;
-  auto take = [&](float e, int i) __attribute__((always_inline)) {
-    nan = nan || (e != e);
-    if (e == e) keep_better(best, idx, e, i);
-  };
   const bool vec = (a.V % 4 == 0) && ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
   if (vec) {
     // float4 columns [lo, hi) of the row.  The kArgmaxUnroll loads of a pass are issued
-    // back to back as inline assembly and waited for once (the compiler would otherwise
-    // wait for some before issuing the rest); loads past hi read column lo again (in
-    // bounds) and are not compared.  A pass is reduced without branches: its maximum over
-    // the valid values (v_max_f32 leaves a quiet NaN operand out; NaNs are flagged on the
-    // side and fail the round), then the lowest index holding that maximum, then one
-    // comparison with the running pair.
+    // back to back as inline assembly (loads past hi read column lo again, in bounds, and
+    // are not compared), and each is taken as soon as it has landed, so that the compares
+    // overlap the rest of the stream.  Per load: its maximum (v_max_f32 leaves a quiet NaN
+    // out; NaNs are flagged on the side and fail the round), kept with the load's four
+    // values when it beats the pass's best so far (strictly: an equal value in a later load
+    // has a larger index); at the end of the pass the lowest column of the kept load that
+    // holds the maximum gives the index.
     const float4* row4 = reinterpret_cast<const float4*>(row);
     const int n4 = a.V / 4;
     const int lo = min(n4, piece * a.chunk4), hi = min(n4, lo + a.chunk4);
@@ -157,72 +176,68 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(AcceptArgs a) {
         const int c = c0 + k * kArgmaxThreads;
         x[k] = load_f32x4(row4 + (c < hi ? c : lo));
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int k = 0; k < kArgmaxUnroll; ++k) asm volatile("" : "+v"(x[k]));
       float pm = -INFINITY;
+      int pk = 0;
+      f32x4 px = {0.f, 0.f, 0.f, 0.f};
       bool pnan = false;
-      int pi = INT_MAX;
-      if (c0 + (kArgmaxUnroll - 1) * kArgmaxThreads < hi) {  // the whole pass is in range
 #pragma unroll
-        for (int k = 0; k < kArgmaxUnroll; ++k)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pnan |= x[k][j] != x[k][j];
-            pm = vmax(pm, x[k][j]);
-          }
-#pragma unroll
-        for (int k = kArgmaxUnroll - 1; k >= 0; --k)
-#pragma unroll
-          for (int j = 3; j >= 0; --j) pi = x[k][j] == pm ? 4 * (c0 + k * kArgmaxThreads) + j : pi;
-      } else {
-#pragma unroll
-        for (int k = 0; k < kArgmaxUnroll; ++k) {
-          const bool ok = c0 + k * kArgmaxThreads < hi;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float e = ok ? x[k][j] : -INFINITY;
-            pnan |= e != e;
-            pm = vmax(pm, e);
-          }
-        }
-#pragma unroll
-        for (int k = kArgmaxUnroll - 1; k >= 0; --k) {
-          const int c = c0 + k * kArgmaxThreads;
-#pragma unroll
-          for (int j = 3; j >= 0; --j) pi = (c < hi && x[k][j] == pm) ? 4 * c + j : pi;
+      for (int k = 0; k < kArgmaxUnroll; ++k) {
+        wait_loads(kArgmaxUnroll - 1 - k);
+        asm volatile("" : "+v"(x[k]));
+        const float m = vmax(vmax3(x[k][0], x[k][1], x[k][2]), x[k][3]);
+        pnan = pnan || __builtin_isunordered(x[k][0], x[k][1]) || __builtin_isunordered(x[k][2], x[k][3]);
+        if (k == 0) {  // column c0 < hi: always in range
+          pm = m;
+          px = x[0];
+        } else {
+          const bool take = c0 + k * kArgmaxThreads < hi && m > pm;
+          pm = take ? m : pm;
+          pk = take ? k : pk;
+          px = take ? x[k] : px;
         }
       }
+      const int j = px[0] == pm ? 0 : px[1] == pm ? 1 : px[2] == pm ? 2 : 3;
       nan = nan || pnan;
-      if (pi != INT_MAX) keep_better(best, idx, pm, pi);
+      keep_better(best, idx, pm, 4 * (c0 + pk * kArgmaxThreads) + j);
     }
   } else {
     const int chunk = (a.V + a.parts - 1) / a.parts;
     const int lo = min(a.V, piece * chunk), hi = min(a.V, lo + chunk);
-    for (int i = lo + int(threadIdx.x); i < hi; i += kArgmaxThreads) take(row[i], i);
+    for (int i = lo + int(threadIdx.x); i < hi; i += kArgmaxThreads) {
+      const float e = row[i];
+      nan = nan || (e != e);
+      if (e == e) keep_better(best, idx, e, i);
+    }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(best, off, 64);
-    const int oi = __shfl_xor(idx, off, 64);
-    keep_better(best, idx, ov, oi);
-  }
+  // the wavefront's maximum, then the lowest index holding it (wavefront reductions on the
+  // data-parallel primitives, not lane shuffles through LDS)
+  const float wm = __ockl_wfred_max_f32(best);
+  const uint32_t wi = __ockl_wfred_min_u32(best == wm ? uint32_t(idx) : 0xffffffffu);
+  const uint32_t wn = __ockl_wfred_or_u32(nan ? 1u : 0u);
   constexpr int kWaves = kArgmaxThreads / 64;
   __shared__ float wv[kWaves];
-  __shared__ int wi[kWaves];
+  __shared__ int wix[kWaves];
+  __shared__ uint32_t wnan[kWaves];
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   if (lane == 0) {
-    wv[wave] = best;
-    wi[wave] = idx;
+    wv[wave] = wm;
+    wix[wave] = int(wi);
+    wnan[wave] = wn;
   }
-  const bool any_nan = __syncthreads_or(nan);
+  __syncthreads();
   if (threadIdx.x == 0 && !failed) {
+    uint32_t any_nan = wnan[0];
+    float v = wv[0];
+    int i = wix[0];
+    for (int w = 1; w < kWaves; ++w) {
+      any_nan |= wnan[w];
+      keep_better(v, i, wv[w], wix[w]);
+    }
     if (any_nan) {
       raise_status(a.status, MEDUSA_EINVAL);
       return;
     }
-    for (int w = 1; w < kWaves; ++w) keep_better(wv[0], wi[0], wv[w], wi[w]);
-    a.part[blockIdx.x] = make_int2(__float_as_int(wv[0]), wi[0]);
+    a.part[blockIdx.x] = make_int2(__float_as_int(v), i);
   }
 }
 
@@ -351,14 +366,33 @@ __device__ __forceinline__ int32_t row_target(const AcceptArgs& a, int b, int u)
   return i;
 }
 
-// One block per sequence.  With kStaged, the tree buffers, this sequence's candidates and
-// the target token of every row are first copied to LDS (all loads issued together), so
-// that the path walks below make no dependent global loads; trees too large for that read
-// them from memory.  The tree buffers must name valid slots and rows, and every retrieve
-// row must start at the root and be padded only at its end; all blocks see the same
-// buffers and reach the same verdict.  kTypical selects the typical edge test (candidate
-// ids must then be tokens of the vocabulary: they index the logits) and ranks paths of
-// equal length by their summed log p.
+// The edge test of one tree edge (the node at row `parent` scores the candidate token c of
+// its child): greedy, c equals the target token of row `parent`; typical, p(c) of that row
+// exceeds tau, with log p(c) returned in ll.  `parent` and c must be in range.
+template <bool kTypical>
+__device__ __forceinline__ bool edge_passes(const AcceptArgs& a, int b, int parent, int c, int32_t tgt_parent,
+                                            float& ll) {
+  if (kTypical) {
+    const int64_t row = int64_t(b) * a.N + parent;
+    const float4 st = a.stats[row];
+    const float pc = __builtin_amdgcn_exp2f(a.logits[row * a.V + c] * a.inv_temperature - st.x) / st.y;
+    const float tau = fminf(a.epsilon, a.alpha * expf(-st.z));
+    ll = __builtin_amdgcn_logf(pc) * kLn2;
+    return pc > tau;
+  }
+  return c == tgt_parent;
+}
+
+// One block per sequence.  The tree buffers must name valid slots and rows, and every
+// retrieve row must start at the root and be padded only at its end; all blocks see the same
+// buffers and reach the same verdict.  kTypical selects the typical edge test (candidate ids
+// must then be tokens of the vocabulary: they index the logits) and ranks paths of equal
+// length by their summed log p.
+// With kStaged the tree buffers, this sequence's candidates and the target token of every
+// row are first copied to LDS, all loads issued together, and each path's edges are then
+// tested side by side rather than one after another along the path (for typical acceptance
+// the logits reads of a path are one batch of loads).  Trees too large for LDS walk each
+// path from memory.
 template <bool kStaged, bool kTypical, bool kCommit = false>
 __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
   const bool failed = round_failed(a.status);  // gates the stores only
@@ -366,20 +400,31 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
   // the committed length is read with the first loads, not after the path walk: only this
   // block writes it, at the very end
   const int64_t P = kCommit ? a.prefix_len[b] : 0;
-  extern __shared__ int32_t sm[];  // tgt[N], tix[N], cand[n_slots], ret[n_paths][W]
+  extern __shared__ int32_t sm[];  // tgt[N], tix[N], cand[n_slots], ret[nret]
   const int32_t* tix = a.tree_indices;
   const int32_t* cand = a.candidates + int64_t(b) * a.n_slots;
   const int32_t* ret = a.retrieve;
+  const int t = int(threadIdx.x), nret = a.n_paths * a.W;
+  bool ok = true;
+  // this thread's candidate path: (length, summed log p, index), compared lexicographically
+  int best_len = -1, best_i = INT_MAX;
+  float best_ll = -INFINITY;
+  auto better = [](int l, float ll, int i, int bl, float bll, int bi) {
+    return l > bl || (l == bl && (ll > bll || (ll == bll && i < bi)));
+  };
+  if (kTypical)  // every sequence's candidates, so that all blocks reach the same verdict
+    for (int i = t; i < a.B * a.n_slots; i += blockDim.x)
+      ok = ok && a.candidates[i] >= 0 && a.candidates[i] < a.V;
   if (kStaged) {
     int32_t* s_tgt = sm;
     int32_t* s_tix = s_tgt + a.N;
     int32_t* s_cand = s_tix + a.N;
     int32_t* s_ret = s_cand + a.n_slots;
-    // The first blockDim.x entries of every array come in one batch: each thread loads
-    // its entry of each (an index past the end is clamped, in bounds, and not stored) and
-    // all the piece results of its row's target, and nothing is stored to LDS before all
-    // of them are issued.  Larger arrays finish in the loops after.
-    const int t = int(threadIdx.x), nret = a.n_paths * a.W;
+    // The first blockDim.x entries of every array come in one batch: each thread loads its
+    // entry of each (an index past the end is clamped, in bounds, and not stored) and all
+    // the piece results of its row's target, and nothing is stored to LDS before all of
+    // them are issued.  Each entry is range-checked as it arrives.  Larger arrays finish in
+    // the loops after.
     const int tu = min(t, a.N - 1);
     const int32_t v_tix = tix[tu];
     const int32_t v_cand = cand[min(t, a.n_slots - 1)];
@@ -402,113 +447,151 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
         v_tgt = a.target_ids[row];
       }
     }
+    auto ret_ok = [&](int e, int32_t v) __attribute__((always_inline)) {
+      return v >= -1 && v < a.N && (e % a.W != 0 || v == 0);  // in range; the root first
+    };
     if (t < a.N) {
       if (!kTypical) s_tgt[t] = v_tgt;
       s_tix[t] = v_tix;
+      ok = ok && v_tix >= 0 && v_tix < a.n_slots;
     }
     if (t < a.n_slots) s_cand[t] = v_cand;
-    if (t < nret) s_ret[t] = v_ret;
+    if (t < nret) {
+      s_ret[t] = v_ret;
+      ok = ok && ret_ok(t, v_ret);
+    }
     for (int u = t + int(blockDim.x); u < a.N; u += blockDim.x) {
       if (!kTypical) s_tgt[u] = row_target(a, b, u);
-      s_tix[u] = tix[u];
+      const int32_t v = tix[u];
+      s_tix[u] = v;
+      ok = ok && v >= 0 && v < a.n_slots;
     }
     for (int i = t + int(blockDim.x); i < a.n_slots; i += blockDim.x) s_cand[i] = cand[i];
-    for (int i = t + int(blockDim.x); i < nret; i += blockDim.x) s_ret[i] = ret[i];
+    for (int e = t + int(blockDim.x); e < nret; e += blockDim.x) {
+      const int32_t v = ret[e];
+      s_ret[e] = v;
+      ok = ok && ret_ok(e, v);
+    }
     __syncthreads();
+    // Every path's run of passing edges from the root, one thread per path: the path's
+    // entries are taken eight at a time and the edge tests of all eight issued together
+    // (for typical acceptance, one batch of logits loads).  A padded entry fails its edge,
+    // and an entry after padding is invalid (padding only at a row's end).
+    for (int i = t; i < a.n_paths; i += blockDim.x) {
+      const int32_t* r = s_ret + i * a.W;
+      int len = 0;
+      float ll = 0.f;
+      bool run = true;
+      int32_t prev = r[0];
+      for (int j0 = 1; j0 < a.W; j0 += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = j0 + k < a.W ? r[j0 + k] : -1;
+        bool pass[8];
+        float el[8];
+        // branch-free, so that the reads of all eight edges are in flight together: indices
+        // are clamped into range and the edge fails where one was not (a slot out of range
+        // also fails the round below)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int32_t parent = k == 0 ? prev : v[k - 1], child = v[k];
+          ok = ok && !(parent < 0 && child >= 0);
+          const int32_t slot = s_tix[max(child, 0)];
+          const bool live = child >= 0 && parent >= 0 && slot >= 0 && slot < a.n_slots;
+          const int32_t c = s_cand[min(max(slot, 0), a.n_slots - 1)];
+          const bool e = edge_passes<kTypical>(a, b, max(parent, 0), kTypical ? min(max(c, 0), a.V - 1) : c,
+                                               kTypical ? 0 : s_tgt[max(parent, 0)], el[k]);
+          pass[k] = live && e;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          run = run && pass[k];
+          if (run) {
+            ++len;
+            if (kTypical) ll += el[k];
+          }
+        }
+        prev = v[7];
+      }
+      if (better(len, ll, i, best_len, best_ll, best_i)) {
+        best_len = len;
+        best_ll = ll;
+        best_i = i;
+      }
+    }
+    if (!__syncthreads_and(ok)) {
+      if (t == 0 && b == 0 && !failed) raise_status(a.status, MEDUSA_EINVAL);
+      return;
+    }
     tix = s_tix;
     cand = s_cand;
     ret = s_ret;
-  }
-  auto tgt = [&](int u) __attribute__((always_inline)) { return kStaged ? sm[u] : row_target(a, b, u); };
-
-  bool ok = true;
-  for (int u = threadIdx.x; u < a.N; u += blockDim.x) ok = ok && tix[u] >= 0 && tix[u] < a.n_slots;
-  if (kTypical)  // every sequence's candidates, so that all blocks reach the same verdict
-    for (int i = threadIdx.x; i < a.B * a.n_slots; i += blockDim.x)
-      ok = ok && a.candidates[i] >= 0 && a.candidates[i] < a.V;
-  for (int i = threadIdx.x; i < a.n_paths; i += blockDim.x) {
-    const int32_t* r = ret + int64_t(i) * a.W;
-    ok = ok && r[0] == 0;
-    bool ended = false;
-    for (int j = 0; j < a.W; ++j) {
-      const int v = r[j];
-      ok = ok && v >= -1 && v < a.N && !(ended && v != -1);
-      ended = ended || v == -1;
-    }
-  }
-  if (!__syncthreads_and(ok)) {
-    if (threadIdx.x == 0 && blockIdx.x == 0 && !failed) raise_status(a.status, MEDUSA_EINVAL);
-    return;
-  }
-
-  // (length, summed log p, -index), compared lexicographically; greedy paths carry 0
-  auto better = [](int l, float ll, int i, int bl, float bll, int bi) {
-    return l > bl || (l == bl && (ll > bll || (ll == bll && i < bi)));
-  };
-  int best_len = -1, best_i = INT_MAX;
-  float best_ll = -INFINITY;
-  for (int i = threadIdx.x; i < a.n_paths; i += blockDim.x) {
-    const int32_t* r = ret + int64_t(i) * a.W;
-    int len = 0;
-    float ll = 0.f;
-    for (int j = 0; j + 1 < a.W; ++j) {
-      const int nxt = r[j + 1];
-      if (nxt < 0) break;
-      const int c = cand[tix[nxt]];
-      if (kTypical) {
-        const int64_t row = int64_t(b) * a.N + r[j];
-        const float4 st = a.stats[row];
-        const float pc = __builtin_amdgcn_exp2f(a.logits[row * a.V + c] * a.inv_temperature - st.x) / st.y;
-        const float tau = fminf(a.epsilon, a.alpha * expf(-st.z));
-        if (!(pc > tau)) break;
-        ll += __builtin_amdgcn_logf(pc) * kLn2;
-      } else if (c != tgt(r[j])) {
-        break;
+  } else {
+    for (int u = t; u < a.N; u += blockDim.x) ok = ok && tix[u] >= 0 && tix[u] < a.n_slots;
+    for (int i = t; i < a.n_paths; i += blockDim.x) {
+      const int32_t* r = ret + int64_t(i) * a.W;
+      ok = ok && r[0] == 0;
+      bool ended = false;
+      for (int j = 0; j < a.W; ++j) {
+        const int v = r[j];
+        ok = ok && v >= -1 && v < a.N && !(ended && v != -1);
+        ended = ended || v == -1;
       }
-      ++len;
     }
-    if (better(len, ll, i, best_len, best_ll, best_i)) {
-      best_len = len;
-      best_ll = ll;
-      best_i = i;
+    if (!__syncthreads_and(ok)) {
+      if (t == 0 && b == 0 && !failed) raise_status(a.status, MEDUSA_EINVAL);
+      return;
+    }
+    for (int i = t; i < a.n_paths; i += blockDim.x) {
+      const int32_t* r = ret + int64_t(i) * a.W;
+      int len = 0;
+      float ll = 0.f;
+      for (int j = 0; j + 1 < a.W; ++j) {
+        const int nxt = r[j + 1];
+        if (nxt < 0) break;
+        float e_ll = 0.f;
+        if (!edge_passes<kTypical>(a, b, r[j], cand[tix[nxt]], kTypical ? 0 : row_target(a, b, r[j]), e_ll)) break;
+        ll += e_ll;
+        ++len;
+      }
+      if (better(len, ll, i, best_len, best_ll, best_i)) {
+        best_len = len;
+        best_ll = ll;
+        best_i = i;
+      }
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const int ol = __shfl_xor(best_len, off, 64);
-    const float oll = __shfl_xor(best_ll, off, 64);
-    const int oi = __shfl_xor(best_i, off, 64);
-    if (better(ol, oll, oi, best_len, best_ll, best_i)) {
-      best_len = ol;
-      best_ll = oll;
-      best_i = oi;
-    }
-  }
+
+  // the block's best path: per wavefront the longest length, then the largest summed log p
+  // among those, then the lowest index (wavefront reductions), then over the wavefronts
+  const int wl = __ockl_wfred_max_i32(best_len);
+  const float wll = kTypical ? __ockl_wfred_max_f32(best_len == wl ? best_ll : -INFINITY) : 0.f;
+  const uint32_t wi =
+      __ockl_wfred_min_u32(best_len == wl && (!kTypical || best_ll == wll) ? uint32_t(best_i) : 0xffffffffu);
   __shared__ int sl[4], si[4];
   __shared__ float sll[4];
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wave = t / 64, lane = t % 64;
   if (lane == 0) {
-    sl[wave] = best_len;
-    sll[wave] = best_ll;
-    si[wave] = best_i;
+    sl[wave] = wl;
+    sll[wave] = wll;
+    si[wave] = int(wi);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < int(blockDim.x / 64); ++w) {
-      if (better(sl[w], sll[w], si[w], sl[0], sll[0], si[0])) {
-        sl[0] = sl[w];
-        sll[0] = sll[w];
-        si[0] = si[w];
+  int alen = sl[0], best = si[0];
+  {
+    float bll = sll[0];
+    for (int w = 1; w < int(blockDim.x / 64); ++w)
+      if (better(sl[w], sll[w], si[w], alen, bll, best)) {
+        alen = sl[w];
+        bll = sll[w];
+        best = si[w];
       }
-    }
   }
-  __syncthreads();
   if (failed) return;
-  const int alen = sl[0], best = si[0];
   const int32_t* r = ret + int64_t(best) * a.W;
-  for (int j = threadIdx.x; j < a.W; j += blockDim.x)
+  for (int j = t; j < a.W; j += blockDim.x)
     a.accepted[int64_t(b) * a.W + j] = j <= alen ? cand[tix[r[j]]] : -1;
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     a.best_path[b] = best;
     a.accept_len[b] = alen;
     a.frontier[b] = r[alen];
@@ -525,41 +608,50 @@ __global__ __launch_bounds__(256) void select_kernel(AcceptArgs a) {
     u32x4 hv[kHiddenRegs];
 #pragma unroll
     for (int k = 0; k < kHiddenRegs; ++k) {
-      const int i = int(threadIdx.x) + k * int(blockDim.x);
+      const int i = t + k * int(blockDim.x);
       if (i < hchunks) hv[k] = *reinterpret_cast<const u32x4*>(hs + 16 * i);
     }
+    // staged row j of the winning path moves to row P + j from row P + r[j]; a row already in
+    // place (r[j] = j, always so for the root) is left alone, so a round that accepts no
+    // candidate moves nothing
     int32_t src[kCommitWidth];
+    bool moves = false;
 #pragma unroll
-    for (int j = 0; j < kCommitWidth; ++j) src[j] = r[j < G ? j : 0];
-    const int cpr = a.row_bytes >> 4;  // 16-byte columns per row
-    const int per_layer = a.Hkv * 2 * cpr;
-    const int items = a.n_layers * per_layer;
-    // column it of (layer, kv head, matrix): all G source rows are read before any
-    // destination row is written (the rows past G re-read row r[0] and are not stored)
-    for (int it = threadIdx.x; it < items; it += blockDim.x) {
-      const int l = it / per_layer, rem = it - l * per_layer;
-      const int g = rem / (2 * cpr), rem2 = rem - g * 2 * cpr;
-      const int m = rem2 / cpr, c = rem2 - m * cpr;
-      unsigned char* base = static_cast<unsigned char*>(m ? a.vc[l] : a.kc[l]) +
-                            ((int64_t(b) * a.Hkv + g) * a.S_max + P) * a.row_bytes + 16 * c;
-      u32x4 v[kCommitWidth];
+    for (int j = 0; j < kCommitWidth; ++j) {
+      src[j] = j < G ? r[j] : j;
+      moves = moves || src[j] != j;
+    }
+    if (moves) {
+      const int cpr = a.row_bytes >> 4;  // 16-byte columns per row
+      const int per_layer = a.Hkv * 2 * cpr;
+      const int items = a.n_layers * per_layer;
+      // column it of (layer, kv head, matrix): every source row is read before any
+      // destination row is written
+      for (int it = t; it < items; it += blockDim.x) {
+        const int l = it / per_layer, rem = it - l * per_layer;
+        const int g = rem / (2 * cpr), rem2 = rem - g * 2 * cpr;
+        const int m = rem2 / cpr, c = rem2 - m * cpr;
+        unsigned char* base = static_cast<unsigned char*>(m ? a.vc[l] : a.kc[l]) +
+                              ((int64_t(b) * a.Hkv + g) * a.S_max + P) * a.row_bytes + 16 * c;
+        u32x4 v[kCommitWidth];
 #pragma unroll
-      for (int j = 0; j < kCommitWidth; ++j)
-        v[j] = *reinterpret_cast<const u32x4*>(base + int64_t(src[j]) * a.row_bytes);
+        for (int j = 0; j < kCommitWidth; ++j)
+          if (src[j] != j) v[j] = *reinterpret_cast<const u32x4*>(base + int64_t(src[j]) * a.row_bytes);
 #pragma unroll
-      for (int j = 0; j < kCommitWidth; ++j)
-        if (j < G) *reinterpret_cast<u32x4*>(base + int64_t(j) * a.row_bytes) = v[j];
+        for (int j = 0; j < kCommitWidth; ++j)
+          if (src[j] != j) *reinterpret_cast<u32x4*>(base + int64_t(j) * a.row_bytes) = v[j];
+      }
     }
 #pragma unroll
     for (int k = 0; k < kHiddenRegs; ++k) {
-      const int i = int(threadIdx.x) + k * int(blockDim.x);
+      const int i = t + k * int(blockDim.x);
       if (i < hchunks) *reinterpret_cast<u32x4*>(hd + 16 * i) = hv[k];
     }
-    for (int i = int(threadIdx.x) + kHiddenRegs * int(blockDim.x); i < hchunks; i += blockDim.x)
+    for (int i = t + kHiddenRegs * int(blockDim.x); i < hchunks; i += blockDim.x)
       *reinterpret_cast<u32x4*>(hd + 16 * i) = *reinterpret_cast<const u32x4*>(hs + 16 * i);
-    __syncthreads();  // every thread has read P
-    if (threadIdx.x == 0) {
-      if (a.next_root) a.next_root[b] = tgt(fr);
+    // every thread read P before the first barrier (which waits for its loads)
+    if (t == 0) {
+      if (a.next_root) a.next_root[b] = kStaged ? sm[fr] : row_target(a, b, fr);
       a.prefix_len[b] = int32_t(P + G);
     }
   }

@@ -244,12 +244,6 @@ __device__ __forceinline__ uint32_t load_b32(const void* p) {
   asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
   return v;
 }
-// the status word, read past the caches like a relaxed system-scope atomic load
-__device__ __forceinline__ uint32_t load_b32_coherent(const void* p) {
-  uint32_t v;
-  asm volatile("global_load_dword %0, %1, off sc0 sc1" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
 template <typename T>
 __device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
 
@@ -292,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int u_q = live ? rq / p.group : 0;
   const int h_q = kvh * p.group + (live ? rq % p.group : 0);
   const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t(b) * N + u_q) * a.Hq + h_q) * kD;
-  uint32_t st_word = load_b32_coherent(a.status);
+  uint32_t st_word = load_b32(a.status);  // written by earlier kernels only: a plain load
   u32x4 raw[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) raw[s] = load_b128(qr + 16 * s + 8 * half);

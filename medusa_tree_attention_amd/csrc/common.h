@@ -23,10 +23,12 @@ template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
 
 // The sticky device status word: non-zero means an earlier step of the round
-// failed and nothing more may be stored.
-__device__ __forceinline__ bool round_failed(const int32_t* status) {
-  return __atomic_load_n(status, __ATOMIC_RELAXED) != 0;
-}
+// failed and nothing more may be stored.  Earlier steps are earlier kernels of the stream
+// (or the host before them), whose writes stream order makes visible to a plain load.  A
+// system-scope atomic load would send every wavefront's read of this one word past the
+// caches to memory, where they queue behind each other (several microseconds at the start
+// of a kernel of a thousand workgroups).
+__device__ __forceinline__ bool round_failed(const int32_t* status) { return *status != 0; }
 
 // First error wins; later ones leave the code unchanged.
 __device__ __forceinline__ void raise_status(int32_t* status, int32_t code) {
