@@ -285,11 +285,29 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const bool live = rq < p.rows;
   const int u_q = live ? rq / p.group : 0;
   const int h_q = kvh * p.group + (live ? rq % p.group : 0);
-  const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t(b) * N + u_q) * a.Hq + h_q) * kD;
   uint32_t st_word = load_b32(a.status);  // written by earlier kernels only: a plain load
-  u32x4 raw[8];
+  // The query rows of the workgroup are fetched once (not once per key phase) by direct
+  // loads into the two ring slots that no stage occupies before the first steady step:
+  // wavefront (rb, kp) fetches rows 16 kp .. 16 kp + 15 of row block rb, four whole
+  // 256-byte rows per instruction, swizzled like the key tiles (lane l lands at chunk l % 16
+  // of its row and fetches logical chunk (l % 16) ^ key(row)).  Each wavefront reads its
+  // 32 rows back in operand order after the set-up barrier.  Rows past the block repeat
+  // the first row of the sequence and are zeroed after the read.
+  unsigned char* const q_stage = s_ring[kRing - 2] + rb * (kRowsWave * kD * 2);
+  {
+    const bf16* qseq = static_cast<const bf16*>(a.q) + int64_t(b) * N * a.Hq * kD;
+    const uint32_t dst = lds_addr(q_stage) + 256 * 16 * kp;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) raw[s] = load_b128(qr + 16 * s + 8 * half);
+    for (int h = 0; h < 4; ++h) {
+      const int rt = 16 * kp + 4 * h + (lane >> 4);
+      const int rr = row0 + rt;
+      const bool lv = rr < p.rows;
+      const int u = lv ? rr / p.group : 0;
+      const int hh = kvh * p.group + (lv ? rr % p.group : 0);
+      const int c = (lane & 15) ^ swz_key(rt);
+      dma16(qseq, uint32_t(((u * a.Hq + hh) * kD + 8 * c) * 2), dst + 1024 * h);
+    }
+  }
   uint32_t dep_q_w = load_b32(a.depth + u_q);
   uint32_t dep0_w = load_b32(a.depth + min(tid, N - 1));
   uint32_t P_lane_w = load_b32(a.prefix_len + min(lane, a.B - 1));  // sequences 0..63, checked below
@@ -402,6 +420,11 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // per thread: (d, tid % 64) with d = tid / 64.  Deeper phases, which few trees need, are
   // formed once the node depths are known.
   static_assert(kThreads == kEarlyDepth * (kD / 2), "one early phase entry per thread");
+  // the query staging (one 8 KiB block per row block) fits the two ring slots that the
+  // stages in flight before the first steady step (0 .. S-2) leave free
+  static_assert((kWaves / kKeyPhases) * kRowsWave * kD * 2 <= 2 * kTileBytes &&
+                    (kRing / kKeyPhases - 1) * kKeyPhases <= kRing - 2,
+                "query staging overlaps the ring");
   const double theta = exp2(-double(tid % (kD / 2)) * (2.0 / kD) * p.log2_base);
   auto phase = [&](int d) __attribute__((always_inline)) {
     const double x = double(P + d) * theta;
@@ -418,8 +441,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   pin(dep_q_w);
   pin(dep0_w);
   pin(P_lane_w);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) pin(raw[s]);
 #pragma unroll
   for (int k = 0; k < kMaskLds / 2; ++k) pin(mword[k]);
   const int dep_q = int(dep_q_w), dep0 = int(dep0_w);
@@ -443,10 +464,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     wait_vm(0);
     if (blockIdx.x == 0 && tid == 0) raise_status(a.status, MEDUSA_ECAPACITY);
     return;
-  }
-  if (!live) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) raw[s] = u32x4{0u, 0u, 0u, 0u};
   }
   bool bad = tid < N && (dep0 < 0 || dep0 >= kTableDepth);
   bool deep = tid < N && dep0 >= kEarlyDepth;
@@ -479,6 +496,10 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // ---- this wavefront's 32 query rows: rotated, scaled to log2 units, bf16 B operands;
   // lane holds query column l32, dims 16 s + 8 half + e (e < 8)
   const float qscale = kLog2e / sqrtf(float(kD));
+  u32x4 raw[8];  // dims 16 s + 8 half .. + 7 of row l32: logical chunk 2 s + half
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    raw[s] = live ? *reinterpret_cast<const u32x4*>(q_stage + swz(l32, 2 * s + half)) : u32x4{0u, 0u, 0u, 0u};
   bf16x8 qhi[8], qlo[8];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -984,8 +1005,9 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
 
 }  // namespace
 
-bool mfma_path_applies(medusa_dtype dt, int32_t, int32_t, int32_t d_h, int32_t) {
-  return dt == MEDUSA_BF16 && d_h == kD;
+bool mfma_path_applies(medusa_dtype dt, int32_t Hq, int32_t, int32_t d_h, int32_t N) {
+  // one sequence's query rows are addressed with 32-bit byte offsets
+  return dt == MEDUSA_BF16 && d_h == kD && int64_t(N) * Hq * kD * 2 <= int64_t(UINT32_MAX);
 }
 
 size_t attn_workspace_bytes(medusa_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d_h,
