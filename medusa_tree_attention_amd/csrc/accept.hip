@@ -44,9 +44,10 @@
 
 #include "common.h"
 
-// the device library's wavefront maximum of a float (declared by the HIP headers only under
-// an opt-in macro)
+// the device library's wavefront maximum and sum of a float (declared by the HIP headers only
+// under an opt-in macro)
 extern "C" __device__ __attribute__((const)) float __ockl_wfred_max_f32(float);
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_add_f32(float);
 
 namespace medusa {
 
@@ -247,16 +248,14 @@ constexpr int kStatCache = 32;  // logits per thread held in registers: rows up 
 constexpr float kLogGuard = 1e-5f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// block-wide reduction of one value per thread (sum or max), the result in every thread
+// block-wide reduction of one value per thread (sum or max), the result in every thread:
+// per wavefront with the data-parallel primitives, then over the wavefronts through LDS.
+// Each reduction of a kernel passes its own scratch (one slot per wavefront), so that one
+// barrier suffices.
 template <bool kMax>
 __device__ __forceinline__ float block_reduce(float v, float* scratch) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float o = __shfl_xor(v, off, 64);
-    v = kMax ? fmaxf(v, o) : v + o;
-  }
+  v = kMax ? __ockl_wfred_max_f32(v) : __ockl_wfred_add_f32(v);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();  // scratch is free
   if (lane == 0) scratch[wave] = v;
   __syncthreads();
   float r = scratch[0];
@@ -272,7 +271,7 @@ __device__ __forceinline__ float block_reduce(float v, float* scratch) {
 template <bool kCached>
 __global__ __launch_bounds__(kStatThreads) void typical_stats_kernel(AcceptArgs a) {
   const bool failed = round_failed(a.status);  // gates the stores only
-  __shared__ float scratch[kStatThreads / 64];
+  __shared__ float scratch[3][kStatThreads / 64];
   const int64_t r = blockIdx.x;
   const float* row = a.logits + r * a.V;
   const int tid = threadIdx.x;
@@ -284,17 +283,21 @@ __global__ __launch_bounds__(kStatThreads) void typical_stats_kernel(AcceptArgs 
     if (vec) {  // thread t holds float4 columns t + 1024 k
       const float4* row4 = reinterpret_cast<const float4*>(row);
       const int n4 = a.V / 4;
+      // every load of the row issued before any is used (each logit is read once: a
+      // nontemporal load), each taken as soon as it has landed
+      f32x4 x[kStatCache / 4];
 #pragma unroll
       for (int k = 0; k < kStatCache / 4; ++k) {
         const int c = tid + k * kStatThreads;
-        // each logit is read once: a nontemporal load
-        const f32x4 x4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row4) + (c < n4 ? c : 0));
-        const float4 x = make_float4(x4[0], x4[1], x4[2], x4[3]);
-        const bool in = c < n4;
-        z[4 * k] = in ? x.x : -INFINITY;
-        z[4 * k + 1] = in ? x.y : -INFINITY;
-        z[4 * k + 2] = in ? x.z : -INFINITY;
-        z[4 * k + 3] = in ? x.w : -INFINITY;
+        x[k] = load_f32x4(row4 + (c < n4 ? c : 0));
+      }
+#pragma unroll
+      for (int k = 0; k < kStatCache / 4; ++k) {
+        wait_loads(kStatCache / 4 - 1 - k);
+        asm volatile("" : "+v"(x[k]));
+        const bool in = tid + k * kStatThreads < n4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[4 * k + j] = in ? x[k][j] : -INFINITY;
       }
     } else {
 #pragma unroll
@@ -303,29 +306,28 @@ __global__ __launch_bounds__(kStatThreads) void typical_stats_kernel(AcceptArgs 
         z[k] = c < a.V ? row[c] : -INFINITY;
       }
     }
+    // the maximum of the raw logits: 1/T > 0 keeps their order, so M = max(x) / T
     float m = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kStatCache; ++k) {
-      nan = nan || (z[k] != z[k]);
-      z[k] *= a.inv_temperature;
-      m = fmaxf(m, z[k]);
+    for (int k = 0; k < kStatCache; k += 2) {
+      nan = nan || __builtin_isunordered(z[k], z[k + 1]);
+      m = vmax3(m, z[k], z[k + 1]);
     }
-    M = block_reduce<true>(m, scratch);
+    M = block_reduce<true>(m, scratch[0]) * a.inv_temperature;
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < kStatCache; ++k) {
-      z[k] = __builtin_amdgcn_exp2f(z[k] - M);  // padding: 2^-inf = 0
+      z[k] = __builtin_amdgcn_exp2f(fmaf(z[k], a.inv_temperature, -M));  // e = 2^(z - M); padding: 0
       s += z[k];
     }
-    S = block_reduce<false>(s, scratch);
-    const float inv_s = 1.0f / S;
-    float h = 0.f;
+    S = block_reduce<false>(s, scratch[1]);
+    // with p = e / S: sum p log2(p + g) = (1/S) sum e log2(e + g S) - log2 S, one product
+    // and one logarithm per logit
+    const float gs = kLogGuard * S;
+    float t = 0.f;
 #pragma unroll
-    for (int k = 0; k < kStatCache; ++k) {
-      const float pk = z[k] * inv_s;
-      h -= pk * __builtin_amdgcn_logf(pk + kLogGuard);
-    }
-    H = block_reduce<false>(h, scratch) * kLn2;
+    for (int k = 0; k < kStatCache; ++k) t = fmaf(z[k], __builtin_amdgcn_logf(z[k] + gs), t);
+    H = (__builtin_amdgcn_logf(S) - block_reduce<false>(t, scratch[2]) / S) * kLn2;
   } else {
     float m = -INFINITY;
     for (int c = tid; c < a.V; c += kStatThreads) {
@@ -333,17 +335,17 @@ __global__ __launch_bounds__(kStatThreads) void typical_stats_kernel(AcceptArgs 
       nan = nan || (x != x);
       m = fmaxf(m, x * a.inv_temperature);
     }
-    M = block_reduce<true>(m, scratch);
+    M = block_reduce<true>(m, scratch[0]);
     float s = 0.f;
     for (int c = tid; c < a.V; c += kStatThreads) s += __builtin_amdgcn_exp2f(row[c] * a.inv_temperature - M);
-    S = block_reduce<false>(s, scratch);
+    S = block_reduce<false>(s, scratch[1]);
     const float inv_s = 1.0f / S;
     float h = 0.f;
     for (int c = tid; c < a.V; c += kStatThreads) {
       const float pk = __builtin_amdgcn_exp2f(row[c] * a.inv_temperature - M) * inv_s;
       h -= pk * __builtin_amdgcn_logf(pk + kLogGuard);
     }
-    H = block_reduce<false>(h, scratch) * kLn2;
+    H = block_reduce<false>(h, scratch[2]) * kLn2;
   }
   const bool any_nan = __syncthreads_or(nan);
   if (tid == 0 && !failed) {
