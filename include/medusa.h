@@ -183,13 +183,13 @@ medusa_status medusa_tree_budget(const double* rank_hit, int32_t num_heads, int3
  * Supported: d_h in {64, 128}; Hq % Hkv == 0; 1 <= N <= 64*mask_words;
  * dt in {MEDUSA_F32, MEDUSA_BF16}.
  * Workspace: device memory of at least medusa_tree_attn_workspace_size(...)
- * bytes, owned by the caller.  For bf16 with d_h = 128 it receives the partial
+ * bytes, owned by the caller.  For bf16 (d_h 64 or 128) it receives the partial
  * results of the key-range splits ((m, l) and O / l in fp32 per query
  * row and split), merged into out by a second kernel of the same call; no state
  * carries from one call to the next.  Calls sharing a workspace must be ordered
  * (same stream).
  * Device-detected errors (d_status): any P_b < 0 or P_b + N > S_max
- * -> MEDUSA_ECAPACITY; for bf16 with d_h = 128, a depth[u] outside [0, 32)
+ * -> MEDUSA_ECAPACITY; for bf16, a depth[u] outside [0, 32)
  * -> MEDUSA_EUNSUPPORTED (the RoPE phase table holds 32 depths); both with no
  * stores to the cache or out.
  */

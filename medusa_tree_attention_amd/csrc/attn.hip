@@ -13,8 +13,9 @@
 // Two device paths:
 //  * stage + rowwise (this file): one wavefront per query row, fp32 math.
 //    Handles every supported shape and is the fp32 path.
-//  * the MFMA path (attn_mfma.hip) for bf16, d_h = 128: GQA query blocks
-//    against the streamed cache on matrix cores.
+//  * the MFMA path (attn_mfma.hip) for bf16, d_h = 128 and 64 (the latter padded
+//    to the 128-wide layout): GQA query blocks against the streamed cache on
+//    matrix cores.
 
 #include <cmath>
 
@@ -213,7 +214,7 @@ extern "C" medusa_status medusa_tree_attn(void* stream, medusa_dtype dt, int32_t
   a.S_max = S_max;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  if (mfma_path_applies(dt, Hq, Hkv, d_h, N)) return run_mfma(a, s, ev_start, ev_stop);
+  if (mfma_path_applies(dt, Hq, Hkv, d_h, N)) return run_mfma(a, d_h, s, ev_start, ev_stop);
   if (dt == MEDUSA_F32)
     return d_h == 64 ? run_rowwise<float, 64>(a, s, ev_start, ev_stop)
                      : run_rowwise<float, 128>(a, s, ev_start, ev_stop);

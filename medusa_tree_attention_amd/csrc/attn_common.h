@@ -48,6 +48,6 @@ constexpr size_t kAttnWorkspaceMax = size_t(256) * 128 * (8 + 128 * 4);
 bool mfma_path_applies(medusa_dtype dt, int32_t Hq, int32_t Hkv, int32_t d_h, int32_t N);
 size_t attn_workspace_bytes(medusa_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d_h,
                             int32_t N, int32_t S_max);
-medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev_stop);
+medusa_status run_mfma(AttnArgs& a, int32_t d_h, hipStream_t stream, void* ev_start, void* ev_stop);
 
 }  // namespace medusa

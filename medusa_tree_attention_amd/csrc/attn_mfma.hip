@@ -1,4 +1,4 @@
-// Matrix-core tree attention for bf16, d_h = 128 (gfx950).
+// Matrix-core tree attention for bf16, d_h = 128 and 64 (gfx950).
 //
 // What is computed is the tree attention of [M7.2] = "M7.2 - Medusa: Multi-Head
 // Candidates, Tree Attention, and Verification", §0x03A/§0x03C (position
@@ -63,7 +63,7 @@
 namespace medusa {
 namespace {
 
-constexpr int kD = 128;          // head dimension
+constexpr int kD = 128;          // head dimension of the LDS and operand layout (d_h = 64 is padded to it)
 constexpr int kTile = 32;        // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -121,7 +121,7 @@ static_assert(size_t(kTargetWGs) * (kRowsWave * kWaves / kKeyPhases) * (sizeof(f
                   kAttnWorkspaceMax,
               "the split partials of the largest plan fit the stated workspace bound");
 
-Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
+Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_h, int32_t N, int32_t S_max) {
   Plan p{};
   p.units = B * Hkv;
   p.group = Hq / Hkv;
@@ -140,7 +140,7 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t S_max) {
   p.xcd_map = p.qblocks > 1 && (int64_t(p.units) * p.splits) % 8 == 0;
   const size_t slots = size_t(p.units) * p.qblocks * p.splits * p.qrows;
   p.o_offset = (slots * sizeof(float2) + 255) / 256 * 256;
-  p.bytes = p.splits > 1 ? p.o_offset + slots * kD * sizeof(float) : 256;
+  p.bytes = p.splits > 1 ? p.o_offset + slots * size_t(d_h) * sizeof(float) : 256;
   return p;
 }
 
@@ -153,6 +153,24 @@ __device__ __forceinline__ int swz_key(int row) { return ((row & 3) << 2) | ((ro
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 256 + ((chunk ^ swz_key(row)) << 4);
 }
+
+// Head dimension d_h = 64 runs on the same layout, padded to kD = 128: dims 0..31 of a row
+// sit in the 16-byte chunks 0..3 and dims 32..63 in chunks 8..11, so that the RoPE pairs
+// (i, i + d_h / 2) of the row are the layout's pairs (j, j + 64) and frequency j of the
+// layout is that of pair i = j.  The other chunks are padding: the query rows hold zeros
+// there (their products with any finite key add nothing), keys and values hold copies of
+// real chunks, and the padded output dims are dropped.  src_chunk gives the chunk of the
+// global row that a layout chunk is fetched from.
+template <int kDH>
+__device__ __forceinline__ int src_chunk(int c) {
+  if constexpr (kDH == kD) return c;
+  else return (c & 8) ? 4 + (c & 3) : (c & 3);
+}
+template <int kDH>
+__device__ __forceinline__ bool real_chunk(int c) { return kDH == kD || (c & 4) == 0; }
+// output dims of accumulator block db (32 layout dims), or -1 for a padded block
+template <int kDH>
+__device__ __forceinline__ int out_block(int db) { return kDH == kD ? 32 * db : ((db & 1) ? -1 : 16 * db); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -247,6 +265,7 @@ __device__ __forceinline__ uint32_t load_b32(const void* p) {
 template <typename T>
 __device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
 
+template <int kDH>
 __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p) {
   const AttnArgs& a = p.a;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -295,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // the first row of the sequence and are zeroed after the read.
   unsigned char* const q_stage = s_ring[kRing - 2] + rb * (kRowsWave * kD * 2);
   {
-    const bf16* qseq = static_cast<const bf16*>(a.q) + int64_t(b) * N * a.Hq * kD;
+    const bf16* qseq = static_cast<const bf16*>(a.q) + int64_t(b) * N * a.Hq * kDH;
     const uint32_t dst = lds_addr(q_stage) + 256 * 16 * kp;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -305,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       const int u = lv ? rr / p.group : 0;
       const int hh = kvh * p.group + (lv ? rr % p.group : 0);
       const int c = (lane & 15) ^ swz_key(rt);
-      dma16(qseq, uint32_t(((u * a.Hq + hh) * kD + 8 * c) * 2), dst + 1024 * h);
+      dma16(qseq, uint32_t(((u * a.Hq + hh) * kDH + 8 * src_chunk<kDH>(c)) * 2), dst + 1024 * h);
     }
   }
   uint32_t dep_q_w = load_b32(a.depth + u_q);
@@ -335,13 +354,13 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   auto tile_start = [&](int i) __attribute__((always_inline)) { return (s_lo + i) * n_kp; };
   auto tile_end = [&](int i) __attribute__((always_inline)) { return min(T, (s_lo + i + 1) * n_kp); };
 
-  const int64_t head = (int64_t(b) * a.Hkv + kvh) * a.S_max * kD;
+  const int64_t head = (int64_t(b) * a.Hkv + kvh) * a.S_max * kDH;
   const bf16* kc = static_cast<const bf16*>(a.k_cache) + head;
   const bf16* vc = static_cast<const bf16*>(a.v_cache) + head;
   bf16* kc_w = static_cast<bf16*>(a.k_cache) + head;
   bf16* vc_w = static_cast<bf16*>(a.v_cache) + head;
-  const bf16* kn = static_cast<const bf16*>(a.k_new) + (int64_t(b) * N * a.Hkv + kvh) * kD;
-  const bf16* vn = static_cast<const bf16*>(a.v_new) + (int64_t(b) * N * a.Hkv + kvh) * kD;
+  const bf16* kn = static_cast<const bf16*>(a.k_new) + (int64_t(b) * N * a.Hkv + kvh) * kDH;
+  const bf16* vn = static_cast<const bf16*>(a.v_new) + (int64_t(b) * N * a.Hkv + kvh) * kDH;
   // LDS buffer of stage i's k-th tile: K at +0, V at +8192
   auto tbuf = [&](int i, int k) __attribute__((always_inline)) -> unsigned char* {
     return s_ring[(i & (S - 1)) * n_kp + k];
@@ -358,23 +377,23 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   for (int h = 0; h < kDmaOps; ++h) {
     rt_dma[h] = kDmaRows * wave + 4 * h + (lane >> 4);
     chunk_dma[h] = (lane & 15) ^ swz_key(rt_dma[h]);  // logical chunk this lane fetches
-    poff[h] = uint32_t(rt_dma[h] * 256 + (chunk_dma[h] << 4));
+    poff[h] = uint32_t(rt_dma[h] * kDH * 2 + (src_chunk<kDH>(chunk_dma[h]) << 4));
   }
   auto issue_tile = [&](int t, unsigned char* buf) __attribute__((always_inline)) {
     const uint32_t lds = lds_addr(buf) + 256 * kDmaRows * wave;
     if ((t + 1) * kTile <= P) {  // full prefix tile
-      const int64_t off = int64_t(t) * kTile * kD;
+      const int64_t off = int64_t(t) * kTile * kDH;
 #pragma unroll
       for (int h = 0; h < kDmaOps; ++h) {
         dma16(kc + off, poff[h], lds + 1024 * h);
         dma16(vc + off, poff[h], lds + 8192 + 1024 * h);
       }
     } else if (t < n_pre) {  // the partial prefix tile: rows past P repeat row 0
-      const int64_t off = int64_t(t) * kTile * kD;
+      const int64_t off = int64_t(t) * kTile * kDH;
 #pragma unroll
       for (int h = 0; h < kDmaOps; ++h) {
         const int r = t * kTile + rt_dma[h] < P ? rt_dma[h] : 0;
-        const uint32_t o = uint32_t(r * 256 + (chunk_dma[h] << 4));
+        const uint32_t o = uint32_t(r * kDH * 2 + (src_chunk<kDH>(chunk_dma[h]) << 4));
         dma16(kc + off, o, lds + 1024 * h);
         dma16(vc + off, o, lds + 8192 + 1024 * h);
       }
@@ -382,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
 #pragma unroll
       for (int h = 0; h < kDmaOps; ++h) {
         const int u = (t - n_pre) * kTile + rt_dma[h];
-        const uint32_t o = uint32_t(((u < N ? u : 0) * a.Hkv * kD + 8 * chunk_dma[h]) * 2);
+        const uint32_t o = uint32_t(((u < N ? u : 0) * a.Hkv * kDH + 8 * src_chunk<kDH>(chunk_dma[h])) * 2);
         dma16(kn, o, lds + 1024 * h);
         dma16(vn, o, lds + 8192 + 1024 * h);
       }
@@ -495,11 +514,12 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
 
   // ---- this wavefront's 32 query rows: rotated, scaled to log2 units, bf16 B operands;
   // lane holds query column l32, dims 16 s + 8 half + e (e < 8)
-  const float qscale = kLog2e / sqrtf(float(kD));
+  const float qscale = kLog2e / sqrtf(float(kDH));
   u32x4 raw[8];  // dims 16 s + 8 half .. + 7 of row l32: logical chunk 2 s + half
 #pragma unroll
   for (int s = 0; s < 8; ++s)
-    raw[s] = live ? *reinterpret_cast<const u32x4*>(q_stage + swz(l32, 2 * s + half)) : u32x4{0u, 0u, 0u, 0u};
+    raw[s] = live && real_chunk<kDH>(2 * s + half) ? *reinterpret_cast<const u32x4*>(q_stage + swz(l32, 2 * s + half))
+                                                  : u32x4{0u, 0u, 0u, 0u};
   bf16x8 qhi[8], qlo[8];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -544,13 +564,13 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     }
     *px = __builtin_bit_cast(uint4, rx);
     *py = __builtin_bit_cast(uint4, ry);
-    if (qb == 0 && uu < N) {
-      bf16* kd = kc_w + (int64_t(P) + uu) * kD;
-      bf16* vd = vc_w + (int64_t(P) + uu) * kD;
+    if (qb == 0 && uu < N && real_chunk<kDH>(c)) {  // layout chunks c, c + 8 hold dims 8 c.., d_h / 2 + 8 c..
+      bf16* kd = kc_w + (int64_t(P) + uu) * kDH;
+      bf16* vd = vc_w + (int64_t(P) + uu) * kDH;
       *reinterpret_cast<uint4*>(kd + 8 * c) = __builtin_bit_cast(uint4, rx);
-      *reinterpret_cast<uint4*>(kd + 8 * c + 64) = __builtin_bit_cast(uint4, ry);
+      *reinterpret_cast<uint4*>(kd + 8 * c + kDH / 2) = __builtin_bit_cast(uint4, ry);
       *reinterpret_cast<uint4*>(vd + 8 * c) = *reinterpret_cast<const uint4*>(buf + 8192 + swz(rt, c));
-      *reinterpret_cast<uint4*>(vd + 8 * c + 64) = *reinterpret_cast<const uint4*>(buf + 8192 + swz(rt, c + 8));
+      *reinterpret_cast<uint4*>(vd + 8 * c + kDH / 2) = *reinterpret_cast<const uint4*>(buf + 8192 + swz(rt, c + 8));
     }
   };
   // once stage i has landed: the staged tiles of the stage get their rows fixed
@@ -778,8 +798,8 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
 #pragma unroll
     for (int e = 0; e < 16; ++e) zero[e] = 0.f;
     // global addresses of the tiles of stage S-1 (issued by step 0); lane offsets in poff[]
-    const bf16* kq = kc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
-    const bf16* vq = vc + int64_t((s_lo + S - 1) * n_kp) * kTile * kD;
+    const bf16* kq = kc + int64_t((s_lo + S - 1) * n_kp) * kTile * kDH;
+    const bf16* vq = vc + int64_t((s_lo + S - 1) * n_kp) * kTile * kDH;
     const uint32_t ring0 = lds_addr(&s_ring[0][0]) + 256 * kDmaRows * wave;
     auto steady = [&](int j, f32x16& sc, f32x16& sn, auto fixed) __attribute__((always_inline)) {
       if constexpr (decltype(fixed)::value) {
@@ -790,11 +810,11 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
         for (int k = 0; k < n_kp; ++k)
 #pragma unroll
           for (int h = 0; h < kDmaOps; ++h) {
-            dma16(kq + k * kTile * kD, poff[h], dst + k * kTileBytes + 1024 * h);
-            dma16(vq + k * kTile * kD, poff[h], dst + k * kTileBytes + 8192 + 1024 * h);
+            dma16(kq + k * kTile * kDH, poff[h], dst + k * kTileBytes + 1024 * h);
+            dma16(vq + k * kTile * kDH, poff[h], dst + k * kTileBytes + 8192 + 1024 * h);
           }
-        kq += n_kp * kTile * kD;
-        vq += n_kp * kTile * kD;
+        kq += n_kp * kTile * kDH;
+        vq += n_kp * kTile * kDH;
       } else {
         wait_stage(j + 1, min(j + S - 2, n_st - 1));
         __syncthreads();
@@ -905,47 +925,53 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // 32 db + 8 g + 4 half + 0..3 in oacc[db][4 g .. 4 g + 3]
   if (p.splits == 1) {
     if (!live) return;
-    bf16* o = static_cast<bf16*>(a.out) + ((int64_t(b) * N + u_q) * a.Hq + h_q) * kD + 4 * half;
+    bf16* o = static_cast<bf16*>(a.out) + ((int64_t(b) * N + u_q) * a.Hq + h_q) * kDH + 4 * half;
     const float inv = 1.0f / lsum;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db) {
+      if (out_block<kDH>(db) < 0) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16& v = oacc[db];
         const bf16x4 ov = {static_cast<bf16>(v[4 * g] * inv), static_cast<bf16>(v[4 * g + 1] * inv),
                            static_cast<bf16>(v[4 * g + 2] * inv), static_cast<bf16>(v[4 * g + 3] * inv)};
-        *reinterpret_cast<bf16x4*>(o + 32 * db + 8 * g) = ov;
+        *reinterpret_cast<bf16x4*>(o + out_block<kDH>(db) + 8 * g) = ov;
       }
+    }
     return;
   }
   // partial of a split: (m, l) and O / l in fp32 (zero for a split that saw no key of the row)
   const int64_t slot = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave + l32;
   if (half == 0) static_cast<float2*>(a.workspace)[slot] = make_float2(m_run, lsum);
-  float* po = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kD + 4 * half;
+  float* po = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kDH + 4 * half;
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db) {
+    if (out_block<kDH>(db) < 0) continue;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x16& v = oacc[db];
-      *reinterpret_cast<float4*>(po + 32 * db + 8 * g) =
+      *reinterpret_cast<float4*>(po + out_block<kDH>(db) + 8 * g) =
           make_float4(v[4 * g] * inv, v[4 * g + 1] * inv, v[4 * g + 2] * inv, v[4 * g + 3] * inv);
     }
+  }
 }
 
 // Merge of the splits: thread (row, 8 dims) combines the splits' partials, weighting split
 // s by l_s 2^(m_s - M).  The splits are visited kGroup at a time (four when there are at
 // most four, else eight) with every load of a group issued before any is used, so that a
 // thread waits for memory once per group rather than once per split.
-constexpr int kMergeRows = 16;  // query rows per 256-thread block: 16 threads per row
+// query rows per 256-thread block: d_h / 8 threads per row
+template <int kDH>
+constexpr int merge_rows() { return 256 / (kDH / 8); }
 
-// Grid: x = unit, y = query block, z = 16-row chunk of the query block, so that every index
-// comes from the launch coordinates without a division by a run-time value.
-template <int kGroup>
+// Grid: x = unit, y = query block, z = chunk of merge_rows() rows of the query block, so that
+// every index comes from the launch coordinates without a division by a run-time value.
+template <int kGroup, int kDH>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   const bool failed = round_failed(p.status);  // gates the store only
-  const int d8 = threadIdx.x & 15;
-  const int r = int(blockIdx.z) * kMergeRows + (threadIdx.x >> 4);  // row of the query block
+  const int d8 = threadIdx.x & (kDH / 8 - 1);
+  const int r = int(blockIdx.z) * merge_rows<kDH>() + int(threadIdx.x) / (kDH / 8);  // row of the query block
   const int qb = int(blockIdx.y), unit = int(blockIdx.x);
   const int row = qb * p.qrows + r;
   if (r >= p.qrows || row >= p.rows) return;
@@ -961,8 +987,8 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
     for (int k = 0; k < kGroup; ++k) {  // slots past the last split re-read split 0
       const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
       mlw[k] = load_b64(p.ml + slot);
-      v[k][0] = load_b128(p.o + slot * kD + 8 * d8);
-      v[k][1] = load_b128(p.o + slot * kD + 8 * d8 + 4);
+      v[k][0] = load_b128(p.o + slot * kDH + 8 * d8);
+      v[k][1] = load_b128(p.o + slot * kDH + 8 * d8 + 4);
     }
     wait_vm(0);
     float2 ml[kGroup];
@@ -996,7 +1022,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   const int b = unit / p.Hkv, kvh = unit - b * p.Hkv;
   const uint32_t u = uint32_t(row) / uint32_t(p.group);
   const int h = kvh * p.group + (row - int(u) * p.group);
-  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kD + 8 * d8;
+  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kDH + 8 * d8;
   bf16x8 ov;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ov[e] = static_cast<bf16>(acc[e] * inv);
@@ -1007,18 +1033,18 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
 
 bool mfma_path_applies(medusa_dtype dt, int32_t Hq, int32_t, int32_t d_h, int32_t N) {
   // one sequence's query rows are addressed with 32-bit byte offsets
-  return dt == MEDUSA_BF16 && d_h == kD && int64_t(N) * Hq * kD * 2 <= int64_t(UINT32_MAX);
+  return dt == MEDUSA_BF16 && (d_h == kD || d_h == kD / 2) && int64_t(N) * Hq * d_h * 2 <= int64_t(UINT32_MAX);
 }
 
 size_t attn_workspace_bytes(medusa_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d_h,
                             int32_t N, int32_t S_max) {
   if (B < 1 || Hkv < 1 || Hq < 1 || N < 1 || S_max < N) return 0;
   if (!mfma_path_applies(dt, Hq, Hkv, d_h, N)) return 256;
-  return make_plan(B, Hq, Hkv, N, S_max).bytes;
+  return make_plan(B, Hq, Hkv, d_h, N, S_max).bytes;
 }
 
-medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev_stop) {
-  const Plan plan = make_plan(a.B, a.Hq, a.Hkv, a.N, a.S_max);
+medusa_status run_mfma(AttnArgs& a, int32_t d_h, hipStream_t stream, void* ev_start, void* ev_stop) {
+  const Plan plan = make_plan(a.B, a.Hq, a.Hkv, d_h, a.N, a.S_max);
   MfmaArgs p{};
   p.a = a;
   p.group = plan.group;
@@ -1029,9 +1055,12 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   p.splits = plan.splits;
   p.xcd_map = plan.xcd_map ? 1 : 0;
   p.o_offset = int64_t(plan.o_offset);
-  p.log2_base = std::log2(a.rope_base);
+  // the layout's frequency j is base^(-2 j / d_h): pair i = j of the head's RoPE
+  p.log2_base = std::log2(a.rope_base) * (double(kD) / d_h);
   const unsigned grid = unsigned(int64_t(plan.units) * plan.splits * plan.qblocks);
-  const void* attn = reinterpret_cast<const void*>(&tree_attn_mfma_kernel);
+  const bool full = d_h == kD;
+  const void* attn = full ? reinterpret_cast<const void*>(&tree_attn_mfma_kernel<kD>)
+                          : reinterpret_cast<const void*>(&tree_attn_mfma_kernel<kD / 2>);
   if (plan.splits == 1) return launch(attn, dim3(grid), dim3(kThreads), 0, stream, p, ev_start, ev_stop);
   const medusa_status st = launch(attn, dim3(grid), dim3(kThreads), 0, stream, p, ev_start, nullptr);
   if (st != MEDUSA_OK) return st;
@@ -1048,9 +1077,13 @@ medusa_status run_mfma(AttnArgs& a, hipStream_t stream, void* ev_start, void* ev
   m.qrows = plan.qrows;
   m.qblocks = plan.qblocks;
   m.splits = plan.splits;
-  const void* merge = plan.splits <= 4 ? reinterpret_cast<const void*>(&tree_attn_merge_kernel<4>)
-                                       : reinterpret_cast<const void*>(&tree_attn_merge_kernel<8>);
-  return launch(merge, dim3(unsigned(plan.units), unsigned(plan.qblocks), unsigned((plan.qrows + kMergeRows - 1) / kMergeRows)),
+  const void* merge =
+      full ? (plan.splits <= 4 ? reinterpret_cast<const void*>(&tree_attn_merge_kernel<4, kD>)
+                               : reinterpret_cast<const void*>(&tree_attn_merge_kernel<8, kD>))
+           : (plan.splits <= 4 ? reinterpret_cast<const void*>(&tree_attn_merge_kernel<4, kD / 2>)
+                               : reinterpret_cast<const void*>(&tree_attn_merge_kernel<8, kD / 2>));
+  const int mrows = full ? merge_rows<kD>() : merge_rows<kD / 2>();
+  return launch(merge, dim3(unsigned(plan.units), unsigned(plan.qblocks), unsigned((plan.qrows + mrows - 1) / mrows)),
                 dim3(256), 0, stream, m, nullptr, ev_stop);
 }
 

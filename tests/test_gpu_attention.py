@@ -58,6 +58,15 @@ EDGE = {
     # matrix-core path with a query block that is not a multiple of 64 rows (N * group = 20)
     "mfma_partial_qtile": (dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=4, Hkv=1,
                                                n_nodes=5), [257, 31]),
+    # d_h = 64 in bf16 on the matrix-core path (padded to the 128-wide layout): the
+    # benchmark's launch shape (four key-range splits and their merge), one split (the
+    # output stored directly), and a 20-deep chain (RoPE frequencies of the shorter head)
+    "mfma_d64_batched": (dataclasses.replace(workloads.WORKLOADS["batched"], d=64), [4096, 4096, 4096, 4096]),
+    "mfma_d64_single_split": (dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=8, Hkv=2, d=64,
+                                                  slack=3), [40, 200]),
+    "mfma_d64_chain": (dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=8, Hkv=2, d=64,
+                                           tree="cartesian", branching=(1,) * 20, num_heads=20, topk=1),
+                       [300, 1000]),
     # a chain: ordinary causal attention over prefix + path
     "chain_f32": (dataclasses.replace(workloads.WORKLOADS["tiny"], Hq=2, Hkv=1, d=128,
                                       branching=(1, 1, 1, 1), num_heads=4, topk=1), [65]),
