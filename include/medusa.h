@@ -184,7 +184,7 @@ medusa_status medusa_tree_budget(const double* rank_hit, int32_t num_heads, int3
  * dt in {MEDUSA_F32, MEDUSA_BF16}.
  * Workspace: device memory of at least medusa_tree_attn_workspace_size(...)
  * bytes, owned by the caller.  For bf16 (d_h 64 or 128) it receives the partial
- * results of the key-range splits ((m, l) and O / l in fp32 per query
+ * results of the key-range splits ((m, l) in fp32 and O / l in 16-bit fixed point per query
  * row and split), merged into out by a second kernel of the same call; no state
  * carries from one call to the next.  Calls sharing a workspace must be ordered
  * (same stream).
@@ -222,7 +222,7 @@ medusa_status medusa_tree_attn(void* stream, medusa_dtype dt, int32_t B, int32_t
  * Errors: those of medusa_tree_attn, plus MEDUSA_EHIP if the array's address cannot be
  * taken on the current GPU.
  */
-#define MEDUSA_TREE_ATTN_SCRATCH_BYTES ((size_t)256 * 128 * (8 + 128 * 4))
+#define MEDUSA_TREE_ATTN_SCRATCH_BYTES ((size_t)256 * 128 * (16 + 128 * 2))
 
 medusa_status medusa_tree_attn_noalloc(void* stream, medusa_dtype dt, int32_t B, int32_t Hq, int32_t Hkv,
                                        int32_t d_h, int32_t N, const int32_t* d_depth,

@@ -41,8 +41,9 @@ __device__ __forceinline__ bool prefixes_fit(const AttnArgs& a) {
 }
 
 // The largest workspace the attention call asks for.  Split partials exist only when the
-// grid has at most 256 workgroups; each holds 128 query rows of (m, l) and 128 fp32 values.
-constexpr size_t kAttnWorkspaceMax = size_t(256) * 128 * (8 + 128 * 4);
+// grid has at most 256 workgroups; each holds 128 query rows of (m, l, s, -) in fp32 and 128
+// 16-bit values.
+constexpr size_t kAttnWorkspaceMax = size_t(256) * 128 * (16 + 128 * 2);
 
 // Host-side dispatch helpers implemented next to the MFMA kernel.
 bool mfma_path_applies(medusa_dtype dt, int32_t Hq, int32_t Hkv, int32_t d_h, int32_t N);

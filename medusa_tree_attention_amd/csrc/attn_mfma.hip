@@ -50,10 +50,11 @@
 //    loaded them, written to cache rows P + u by query block 0, and masked per
 //    lane with the ancestor bitmask.  RoPE phases are reduced modulo 2 pi in
 //    binary64 and evaluated in fp32.
-//  * Splits of one query block are merged by a second, small kernel from
-//    (m, l, O / l) partials kept in fp32 in the workspace (a bf16 partial would add
-//    a second rounding to the output's); with a single split the first kernel
-//    writes the output itself.
+//  * Splits of one query block are merged by a second, small kernel from (m, l)
+//    and O / l partials in the workspace, O / l as 16-bit fixed point scaled by the
+//    row's largest |O / l| (within 2^-16 of it: a bf16 partial would add a second
+//    rounding of the output's size); with a single split the first kernel writes
+//    the output itself.
 
 #include <cmath>
 #include <type_traits>
@@ -104,8 +105,8 @@ struct MfmaArgs {
 };
 
 struct MergeArgs {
-  const float2* ml;  // [units][qblocks][splits][qrows] (m, l)
-  const float* o;    // [units][qblocks][splits][qrows][D], O / l of the split
+  const float4* ml;  // [units][qblocks][splits][qrows] (m, l, s, -): s the row's largest |O / l|
+  const int16_t* o;  // [units][qblocks][splits][qrows][D], O / (l s) in 16-bit fixed point
   void* out;
   const int32_t* status;
   int32_t Hq, Hkv, N, group, rows, qrows, qblocks, splits;
@@ -117,7 +118,7 @@ struct Plan {
   size_t o_offset, bytes;
 };
 
-static_assert(size_t(kTargetWGs) * (kRowsWave * kWaves / kKeyPhases) * (sizeof(float2) + kD * sizeof(float)) <=
+static_assert(size_t(kTargetWGs) * (kRowsWave * kWaves / kKeyPhases) * (sizeof(float4) + kD * sizeof(int16_t)) <=
                   kAttnWorkspaceMax,
               "the split partials of the largest plan fit the stated workspace bound");
 
@@ -139,8 +140,8 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t d_h, int32_t N, int32
   p.splits = splits < 1 ? 1 : splits;
   p.xcd_map = p.qblocks > 1 && (int64_t(p.units) * p.splits) % 8 == 0;
   const size_t slots = size_t(p.units) * p.qblocks * p.splits * p.qrows;
-  p.o_offset = (slots * sizeof(float2) + 255) / 256 * 256;
-  p.bytes = p.splits > 1 ? p.o_offset + slots * size_t(d_h) * sizeof(float) : 256;
+  p.o_offset = (slots * sizeof(float4) + 255) / 256 * 256;
+  p.bytes = p.splits > 1 ? p.o_offset + slots * size_t(d_h) * sizeof(int16_t) : 256;
   return p;
 }
 
@@ -940,19 +941,39 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     }
     return;
   }
-  // partial of a split: (m, l) and O / l in fp32 (zero for a split that saw no key of the row)
+  // Partial of a split: (m, l, s) in fp32 and O / l as 16-bit fixed point relative to s, the
+  // row's largest |O / l| (v_cvt_pknorm_i16_f32: round(x 32767) of x in [-1, 1]), i.e. to
+  // within 2^-16 s of each value -- well inside the bf16 rounding of the output (2^-9 of |o|)
+  // and half the bytes of fp32 partials, which every split writes and the merge reads back.
+  // A split that saw no key of the row stores l = s = 0.
   const int64_t slot = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave + l32;
-  if (half == 0) static_cast<float2*>(a.workspace)[slot] = make_float2(m_run, lsum);
-  float* po = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kDH + 4 * half;
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  float amax = 0.f;  // largest |O| of this lane's dims, then of the row (the two halves)
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    if (out_block<kDH>(db) < 0) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = max2f(amax, fabsf(oacc[db][e]));
+  }
+  {
+    float y0, y1;
+    halves(amax, y0, y1);
+    amax = max2f(y0, y1);
+  }
+  const float sc = lsum > 0.f ? amax / lsum : 0.f;
+  if (half == 0) static_cast<float4*>(a.workspace)[slot] = make_float4(m_run, lsum, sc, 0.f);
+  int16_t* po = reinterpret_cast<int16_t*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kDH + 4 * half;
+  const float k = amax > 0.f ? 1.0f / amax : 0.f;
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     if (out_block<kDH>(db) < 0) continue;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x16& v = oacc[db];
-      *reinterpret_cast<float4*>(po + out_block<kDH>(db) + 8 * g) =
-          make_float4(v[4 * g] * inv, v[4 * g + 1] * inv, v[4 * g + 2] * inv, v[4 * g + 3] * inv);
+      const s16x2 a0 = __builtin_amdgcn_cvt_pknorm_i16(v[4 * g] * k, v[4 * g + 1] * k);
+      const s16x2 a1 = __builtin_amdgcn_cvt_pknorm_i16(v[4 * g + 2] * k, v[4 * g + 3] * k);
+      *reinterpret_cast<u32x2*>(po + out_block<kDH>(db) + 8 * g) =
+          u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)};
     }
   }
 }
@@ -981,23 +1002,20 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   for (int s0 = 0; s0 < p.splits; s0 += kGroup) {
     // issued as inline assembly, every load of the group back to back and then one wait:
     // left to itself the compiler waits for each split's load before it issues the next
-    u32x2 mlw[kGroup];
-    u32x4 v[kGroup][2];
+    u32x4 mlw[kGroup], v[kGroup];
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {  // slots past the last split re-read split 0
       const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
-      mlw[k] = load_b64(p.ml + slot);
-      v[k][0] = load_b128(p.o + slot * kDH + 8 * d8);
-      v[k][1] = load_b128(p.o + slot * kDH + 8 * d8 + 4);
+      mlw[k] = load_b128(p.ml + slot);
+      v[k] = load_b128(p.o + slot * kDH + 8 * d8);
     }
     wait_vm(0);
-    float2 ml[kGroup];
+    float3 ml[kGroup];  // (m, l, s)
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
       pin(mlw[k]);
-      pin(v[k][0]);
-      pin(v[k][1]);
-      ml[k] = make_float2(__uint_as_float(mlw[k][0]), __uint_as_float(mlw[k][1]));
+      pin(v[k]);
+      ml[k] = make_float3(__uint_as_float(mlw[k][0]), __uint_as_float(mlw[k][1]), __uint_as_float(mlw[k][2]));
     }
     float Mg = M;
 #pragma unroll
@@ -1012,8 +1030,12 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
     for (int k = 0; k < kGroup; ++k) {
       const float wt = (s0 + k < p.splits && ml[k].x != -INFINITY) ? ml[k].y * exp2_fast(ml[k].x - Mg) : 0.f;
       L += wt;
+      const float cw = wt * ml[k].z * (1.0f / 32767.0f);  // weight of one fixed-point step
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wt * __uint_as_float(v[k][e >> 2][e & 3]);
+      for (int e = 0; e < 8; ++e) {
+        const int32_t q = int32_t(int16_t(v[k][e >> 1] >> (16 * (e & 1))));
+        acc[e] += cw * float(q);
+      }
     }
     M = Mg;
   }
@@ -1065,8 +1087,8 @@ medusa_status run_mfma(AttnArgs& a, int32_t d_h, hipStream_t stream, void* ev_st
   const medusa_status st = launch(attn, dim3(grid), dim3(kThreads), 0, stream, p, ev_start, nullptr);
   if (st != MEDUSA_OK) return st;
   MergeArgs m{};
-  m.ml = static_cast<const float2*>(a.workspace);
-  m.o = reinterpret_cast<const float*>(static_cast<const unsigned char*>(a.workspace) + plan.o_offset);
+  m.ml = static_cast<const float4*>(a.workspace);
+  m.o = reinterpret_cast<const int16_t*>(static_cast<const unsigned char*>(a.workspace) + plan.o_offset);
   m.out = a.out;
   m.status = a.status;
   m.Hq = a.Hq;

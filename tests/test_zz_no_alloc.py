@@ -54,7 +54,7 @@ def test_noalloc_matches_the_workspace_call_on_consecutive_calls():
 def test_scratch_bound_covers_the_largest_workspace():
     """Every shape's workspace fits the array: partials exist only for grids of at most
     256 workgroups of 128 rows."""
-    bound = 256 * 128 * (8 + 128 * 4)
+    bound = 256 * 128 * (16 + 128 * 2)
     for B, Hq, Hkv, N, P in [(4, 32, 8, 64, 4096), (1, 32, 8, 64, 8192), (1, 32, 32, 341, 4096),
                              (3, 8, 2, 64, 20000), (1, 4, 1, 5, 100000), (2, 64, 1, 64, 1000)]:
         assert M.medusa_tree_attn_workspace_size(M.BF16, B, Hq, Hkv, 128, N, P + N) <= bound
