@@ -445,6 +445,10 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   static_assert((kWaves / kKeyPhases) * kRowsWave * kD * 2 <= 2 * kTileBytes &&
                     (kRing / kKeyPhases - 1) * kKeyPhases <= kRing - 2,
                 "query staging overlaps the ring");
+  // the rotated query operands (16 per row block, 16 bytes per lane) fit the slots of stages
+  // 1 .. S-2, which are issued only once every wavefront has read them
+  static_assert((kWaves / kKeyPhases) * 16 * 64 * 16 <= (kRing - 2 - kKeyPhases) * kTileBytes,
+                "query operands overlap the staging or the first stage");
   const double theta = exp2(-double(tid % (kD / 2)) * (2.0 / kD) * p.log2_base);
   auto phase = [&](int d) __attribute__((always_inline)) {
     const double x = double(P + d) * theta;
@@ -514,29 +518,45 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   }
 
   // ---- this wavefront's 32 query rows: rotated, scaled to log2 units, bf16 B operands;
-  // lane holds query column l32, dims 16 s + 8 half + e (e < 8)
+  // lane holds query column l32, dims 16 s + 8 half + e (e < 8).  The two wavefronts of a row
+  // block (its two key phases) share the rotation: wavefront kp rotates the dim pairs of
+  // s = 2 kp, 2 kp + 1 (dims 16 s.. and their partners 64 + 16 s..) and leaves its hi and lo
+  // operands in LDS, in the ring slots of stages 1 and 2 (issued only after the barrier
+  // below); after the barrier each wavefront reads all sixteen of its row block's operands.
   const float qscale = kLog2e / sqrtf(float(kDH));
-  u32x4 raw[8];  // dims 16 s + 8 half .. + 7 of row l32: logical chunk 2 s + half
+  unsigned char* const q_ops = s_ring[kKeyPhases] + rb * (16 * 64 * 16);  // [operand][lane] x 16 B
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    raw[s] = live && real_chunk<kDH>(2 * s + half) ? *reinterpret_cast<const u32x4*>(q_stage + swz(l32, 2 * s + half))
-                                                  : u32x4{0u, 0u, 0u, 0u};
-  bf16x8 qhi[8], qlo[8];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const bf16x8 lo = __builtin_bit_cast(bf16x8, raw[s]);
-    const bf16x8 hi = __builtin_bit_cast(bf16x8, raw[s + 4]);
+  for (int t = 0; t < 2; ++t) {
+    const int s = 2 * kp + t;
+    const bool real = live && real_chunk<kDH>(2 * s + half);  // its partner chunk 2 s + 8 + half is alike
+    const bf16x8 lo = __builtin_bit_cast(
+        bf16x8, real ? *reinterpret_cast<const u32x4*>(q_stage + swz(l32, 2 * s + half)) : u32x4{0u, 0u, 0u, 0u});
+    const bf16x8 hi = __builtin_bit_cast(
+        bf16x8, real ? *reinterpret_cast<const u32x4*>(q_stage + swz(l32, 2 * s + 8 + half)) : u32x4{0u, 0u, 0u, 0u});
+    bf16x8 h1, h2, l1, l2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float2 cs = s_cs[dep_q][16 * s + 8 * half + e];
       const float x1 = float(lo[e]), x2 = float(hi[e]);
       const float r1 = (x1 * cs.x - x2 * cs.y) * qscale;
       const float r2 = (x2 * cs.x + x1 * cs.y) * qscale;
-      qhi[s][e] = static_cast<bf16>(r1);
-      qhi[s + 4][e] = static_cast<bf16>(r2);
-      qlo[s][e] = static_cast<bf16>(r1 - float(qhi[s][e]));
-      qlo[s + 4][e] = static_cast<bf16>(r2 - float(qhi[s + 4][e]));
+      h1[e] = static_cast<bf16>(r1);
+      h2[e] = static_cast<bf16>(r2);
+      l1[e] = static_cast<bf16>(r1 - float(h1[e]));
+      l2[e] = static_cast<bf16>(r2 - float(h2[e]));
     }
+    // operand o: hi s = o, lo s = 8 + o
+    *reinterpret_cast<u32x4*>(q_ops + (s * 64 + lane) * 16) = __builtin_bit_cast(u32x4, h1);
+    *reinterpret_cast<u32x4*>(q_ops + ((s + 4) * 64 + lane) * 16) = __builtin_bit_cast(u32x4, h2);
+    *reinterpret_cast<u32x4*>(q_ops + ((8 + s) * 64 + lane) * 16) = __builtin_bit_cast(u32x4, l1);
+    *reinterpret_cast<u32x4*>(q_ops + ((12 + s) * 64 + lane) * 16) = __builtin_bit_cast(u32x4, l2);
+  }
+  __syncthreads();  // the row block's operands are in LDS
+  bf16x8 qhi[8], qlo[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qhi[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_ops + (s * 64 + lane) * 16));
+    qlo[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q_ops + ((8 + s) * 64 + lane) * 16));
   }
 
   // Staged rows of one tile that this wavefront loaded (rows kDmaRows w ..): rotate K in
@@ -772,9 +792,9 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int first = min(S - 1, n_st);  // stages in flight ahead of the loop
   if (n_st > 0) {
     wait_stage(0, 0);
-    for (int i = 1; i < first; ++i) issue_stage(i);  // fill the rest of the ring but one slot
     fix_stage(0);
-    __syncthreads();
+    __syncthreads();  // stage 0 visible; every wavefront has read its query operands
+    for (int i = 1; i < first; ++i) issue_stage(i);  // fill the rest of the ring but one slot
     prep(0, s_cur, b_cur);
   }
 
