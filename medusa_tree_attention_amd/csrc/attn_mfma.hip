@@ -105,7 +105,7 @@ struct MfmaArgs {
 };
 
 struct MergeArgs {
-  const float4* ml;  // [units][qblocks][splits][qrows] (m, l, s, -): s the row's largest |O / l|
+  const float4* ml;  // [units][qblocks][splits][qrows] (m, l, s0, s1): largest |O / l| per half
   const int16_t* o;  // [units][qblocks][splits][qrows][D], O / (l s) in 16-bit fixed point
   void* out;
   const int32_t* status;
@@ -910,92 +910,145 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     b_cur = b_nxt;
   }
 
-  // ---- combine the key phases (n_kp = 2: wavefront (rb, 1) hands its state to (rb, 0))
+  // ---- combine the key phases.  The two wavefronts of a row block split the work: wavefront
+  // kp keeps the output dims of accumulator blocks 2 kp and 2 kp + 1 and hands its partner
+  // the other two blocks and its (m, l) through LDS; each then combines and stores its half.
   float lsum;
   {
     float y0, y1;
     halves(l_run, y0, y1);
     lsum = y0 + y1;
   }
-  if (n_kp == 2) {
-    __syncthreads();  // every wavefront is done with the ring
-    float* xo = reinterpret_cast<float*>(&s_ring[0][0]) + rb * (64 * 64 + 2 * 64);
-    if (kp == 1) {
+  static_assert(kKeyPhases == 2, "the epilogue combines two key phases");
+  __syncthreads();  // every wavefront is done with the ring
+  {
+    float* give = reinterpret_cast<float*>(&s_ring[0][0]) + (2 * rb + kp) * (32 * 64 + 2 * 64);
+    const float* take = reinterpret_cast<const float*>(&s_ring[0][0]) + (2 * rb + (kp ^ 1)) * (32 * 64 + 2 * 64);
+    auto hand_over = [&](auto first) __attribute__((always_inline)) {  // blocks first, first + 1
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) xo[(db * 16 + e) * 64 + lane] = oacc[db][e];
-      xo[64 * 64 + lane] = m_run;
-      xo[64 * 64 + 64 + lane] = lsum;
-    }
+        for (int e = 0; e < 16; ++e) give[(j * 16 + e) * 64 + lane] = oacc[decltype(first)::value + j][e];
+    };
+    if (kp == 0)
+      hand_over(std::integral_constant<int, 2>{});
+    else
+      hand_over(std::integral_constant<int, 0>{});
+    give[32 * 64 + lane] = m_run;
+    give[32 * 64 + 64 + lane] = lsum;
     __syncthreads();
-    if (kp == 1) return;
-    const float m1 = xo[64 * 64 + lane], l1 = xo[64 * 64 + 64 + lane];
+    const float m1 = take[32 * 64 + lane], l1 = take[32 * 64 + 64 + lane];
     const float M = fmaxf(m_run, m1);
     const float w0 = m_run == -INFINITY ? 0.f : exp2_fast(m_run - M);
     const float w1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - M);
     lsum = w0 * lsum + w1 * l1;
     m_run = M;
+    auto combine = [&](auto first) __attribute__((always_inline)) {  // blocks first, first + 1
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] = w0 * oacc[db][e] + w1 * xo[(db * 16 + e) * 64 + lane];
+        for (int e = 0; e < 16; ++e)
+          oacc[decltype(first)::value + j][e] =
+              w0 * oacc[decltype(first)::value + j][e] + w1 * take[(j * 16 + e) * 64 + lane];
+    };
+    if (kp == 0)
+      combine(std::integral_constant<int, 0>{});
+    else
+      combine(std::integral_constant<int, 2>{});
   }
 
   // ---- results: lane (half, l32) holds, for query row row0 + l32, dims
-  // 32 db + 8 g + 4 half + 0..3 in oacc[db][4 g .. 4 g + 3]
+  // 32 db + 8 g + 4 half + 0..3 in oacc[db][4 g .. 4 g + 3]; this wavefront stores blocks
+  // 2 kp and 2 kp + 1
   if (p.splits == 1) {
     if (!live) return;
     bf16* o = static_cast<bf16*>(a.out) + ((int64_t(b) * N + u_q) * a.Hq + h_q) * kDH + 4 * half;
     const float inv = 1.0f / lsum;
+    auto store = [&](auto first) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+      for (int db = decltype(first)::value; db < decltype(first)::value + 2; ++db) {
+        if (out_block<kDH>(db) < 0) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& v = oacc[db];
+          const bf16x4 ov = {static_cast<bf16>(v[4 * g] * inv), static_cast<bf16>(v[4 * g + 1] * inv),
+                             static_cast<bf16>(v[4 * g + 2] * inv), static_cast<bf16>(v[4 * g + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(o + out_block<kDH>(db) + 8 * g) = ov;
+        }
+      }
+    };
+    if (kp == 0)
+      store(std::integral_constant<int, 0>{});
+    else
+      store(std::integral_constant<int, 2>{});
+    return;
+  }
+  // Partial of a split: (m, l, s0, s1) in fp32 and O / l as 16-bit fixed point relative to s0
+  // for the dims of blocks 0 and 1 and to s1 for those of blocks 2 and 3: the row's largest
+  // |O / l| over each half (v_cvt_pknorm_i16_f32: round(x 32767) of x in [-1, 1]), i.e. to
+  // within 2^-16 s of each value -- well inside the bf16 rounding of the output (2^-9 of |o|)
+  // and half the bytes of fp32 partials, which every split writes and the merge reads back.
+  // A split that saw no key of the row stores l = s = 0.
+  // The O part is laid out [unit][query block][split][half][query row][d_h / 2]: the rows of a
+  // wavefront's half are one contiguous run, written through LDS (this wavefront's own slice
+  // of the ring, past the exchange areas) as whole 16-byte pieces rather than 8-byte pieces
+  // scattered over 32 rows.
+  const int64_t slot = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave + l32;
+  float* rec = reinterpret_cast<float*>(static_cast<float4*>(a.workspace) + slot);
+  constexpr int kHalfBytes = kDH;               // d_h / 2 int16 values per row and half
+  constexpr int kStgStride = kHalfBytes + 8;    // padded: the lanes' 8-byte writes hit distinct banks
+  unsigned char* const stg = &s_ring[0][0] + 73728 + wave * (kRowsWave * kStgStride);
+  static_assert(73728 >= kWaves * (32 * 64 + 2 * 64) * 4 && 73728 + kWaves * kRowsWave * (kD + 8) <= kRing * kTileBytes,
+                "the store staging lies past the exchange areas, inside the ring");
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  auto store_partial = [&](auto first) __attribute__((always_inline)) {
+    constexpr int f = decltype(first)::value;
+    unsigned char* const oh = static_cast<unsigned char*>(a.workspace) + p.o_offset +
+                              ((((int64_t(unit) * p.qblocks + qb) * p.splits + split) * 2 + f / 2) * p.qrows +
+                               rb * kRowsWave) * kHalfBytes;
+    float amax = 0.f;  // largest |O| of this lane's dims of the half, then of the row's (two lanes)
+#pragma unroll
+    for (int db = f; db < f + 2; ++db) {
+      if (out_block<kDH>(db) < 0) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = max2f(amax, fabsf(oacc[db][e]));
+    }
+    {
+      float y0, y1;
+      halves(amax, y0, y1);
+      amax = max2f(y0, y1);
+    }
+    if (half == 0) {
+      if (f == 0) *reinterpret_cast<float2*>(rec) = make_float2(m_run, lsum);
+      rec[2 + f / 2] = lsum > 0.f ? amax / lsum : 0.f;
+    }
+    const float k = amax > 0.f ? 1.0f / amax : 0.f;
+#pragma unroll
+    for (int db = f; db < f + 2; ++db) {
       if (out_block<kDH>(db) < 0) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16& v = oacc[db];
-        const bf16x4 ov = {static_cast<bf16>(v[4 * g] * inv), static_cast<bf16>(v[4 * g + 1] * inv),
-                           static_cast<bf16>(v[4 * g + 2] * inv), static_cast<bf16>(v[4 * g + 3] * inv)};
-        *reinterpret_cast<bf16x4*>(o + out_block<kDH>(db) + 8 * g) = ov;
+        const s16x2 a0 = __builtin_amdgcn_cvt_pknorm_i16(v[4 * g] * k, v[4 * g + 1] * k);
+        const s16x2 a1 = __builtin_amdgcn_cvt_pknorm_i16(v[4 * g + 2] * k, v[4 * g + 3] * k);
+        // dims out_block(db) + 8 g + 4 half .. + 3 of the row, at their place within the half
+        *reinterpret_cast<u32x2*>(stg + l32 * kStgStride + (out_block<kDH>(db) - out_block<kDH>(f) + 8 * g + 4 * half) * 2) =
+            u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)};
       }
     }
-    return;
-  }
-  // Partial of a split: (m, l, s) in fp32 and O / l as 16-bit fixed point relative to s, the
-  // row's largest |O / l| (v_cvt_pknorm_i16_f32: round(x 32767) of x in [-1, 1]), i.e. to
-  // within 2^-16 s of each value -- well inside the bf16 rounding of the output (2^-9 of |o|)
-  // and half the bytes of fp32 partials, which every split writes and the merge reads back.
-  // A split that saw no key of the row stores l = s = 0.
-  const int64_t slot = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave + l32;
-  float amax = 0.f;  // largest |O| of this lane's dims, then of the row (the two halves)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's staging is complete
+    constexpr int kLanesRow = kHalfBytes / 16, kRowsPass = 64 / kLanesRow;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    if (out_block<kDH>(db) < 0) continue;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) amax = max2f(amax, fabsf(oacc[db][e]));
-  }
-  {
-    float y0, y1;
-    halves(amax, y0, y1);
-    amax = max2f(y0, y1);
-  }
-  const float sc = lsum > 0.f ? amax / lsum : 0.f;
-  if (half == 0) static_cast<float4*>(a.workspace)[slot] = make_float4(m_run, lsum, sc, 0.f);
-  int16_t* po = reinterpret_cast<int16_t*>(static_cast<unsigned char*>(a.workspace) + p.o_offset) + slot * kDH + 4 * half;
-  const float k = amax > 0.f ? 1.0f / amax : 0.f;
-  typedef short s16x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    if (out_block<kDH>(db) < 0) continue;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x16& v = oacc[db];
-      const s16x2 a0 = __builtin_amdgcn_cvt_pknorm_i16(v[4 * g] * k, v[4 * g + 1] * k);
-      const s16x2 a1 = __builtin_amdgcn_cvt_pknorm_i16(v[4 * g + 2] * k, v[4 * g + 3] * k);
-      *reinterpret_cast<u32x2*>(po + out_block<kDH>(db) + 8 * g) =
-          u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)};
+    for (int i = 0; i < kRowsWave / kRowsPass; ++i) {
+      const int row = i * kRowsPass + lane / kLanesRow, c = lane % kLanesRow;
+      *reinterpret_cast<u32x4*>(oh + row * kHalfBytes + 16 * c) =
+          *reinterpret_cast<const u32x4*>(stg + row * kStgStride + 16 * c);
     }
-  }
+  };
+  if (kp == 0)
+    store_partial(std::integral_constant<int, 0>{});
+  else
+    store_partial(std::integral_constant<int, 2>{});
 }
 
 // Merge of the splits: thread (row, 8 dims) combines the splits' partials, weighting split
@@ -1016,7 +1069,9 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   const int qb = int(blockIdx.y), unit = int(blockIdx.x);
   const int row = qb * p.qrows + r;
   if (r >= p.qrows || row >= p.rows) return;
-  const int64_t base = (int64_t(unit) * p.qblocks + qb) * p.splits * p.qrows + r;  // slot of split 0
+  const int64_t grp0 = (int64_t(unit) * p.qblocks + qb) * p.splits;  // (unit, query block, split 0)
+  const int64_t base = grp0 * p.qrows + r;                             // slot of split 0
+  const int hf = 8 * d8 < kDH / 2 ? 0 : 1, din = 8 * d8 - hf * (kDH / 2);  // half and dim within it
   float M = -INFINITY, L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < p.splits; s0 += kGroup) {
@@ -1027,15 +1082,18 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
     for (int k = 0; k < kGroup; ++k) {  // slots past the last split re-read split 0
       const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
       mlw[k] = load_b128(p.ml + slot);
-      v[k] = load_b128(p.o + slot * kDH + 8 * d8);
+      // O of (split, half hf, row r): [..][split][hf][qrows][d_h / 2]
+      const int64_t sp = grp0 + int64_t(s0 + k < p.splits ? s0 + k : 0);
+      v[k] = load_b128(p.o + ((sp * 2 + hf) * p.qrows + r) * (kDH / 2) + din);
     }
     wait_vm(0);
-    float3 ml[kGroup];  // (m, l, s)
+    float4 ml[kGroup];  // (m, l, s0, s1)
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
       pin(mlw[k]);
       pin(v[k]);
-      ml[k] = make_float3(__uint_as_float(mlw[k][0]), __uint_as_float(mlw[k][1]), __uint_as_float(mlw[k][2]));
+      ml[k] = make_float4(__uint_as_float(mlw[k][0]), __uint_as_float(mlw[k][1]), __uint_as_float(mlw[k][2]),
+                          __uint_as_float(mlw[k][3]));
     }
     float Mg = M;
 #pragma unroll
@@ -1050,7 +1108,8 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
     for (int k = 0; k < kGroup; ++k) {
       const float wt = (s0 + k < p.splits && ml[k].x != -INFINITY) ? ml[k].y * exp2_fast(ml[k].x - Mg) : 0.f;
       L += wt;
-      const float cw = wt * ml[k].z * (1.0f / 32767.0f);  // weight of one fixed-point step
+      // weight of one fixed-point step: dims of blocks 0, 1 are relative to s0, the rest to s1
+      const float cw = wt * (8 * d8 < kDH / 2 ? ml[k].z : ml[k].w) * (1.0f / 32767.0f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int32_t q = int32_t(int16_t(v[k][e >> 1] >> (16 * (e & 1))));
