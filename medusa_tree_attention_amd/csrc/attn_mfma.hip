@@ -56,6 +56,7 @@
 //    rounding of the output's size); with a single split the first kernel writes
 //    the output itself.
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -91,6 +92,37 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Indices are divided by run-time divisors without the integer division sequence (about 25
+// instructions, several of them quarter rate; the set-up of a workgroup needs a dozen).
+//
+// Per-lane indices use an fp32 reciprocal.  With r = 1/d rounded up to fp32,
+// trunc(fl(n r)) = floor(n / d) for 0 <= n < kFastDivMax and d <= kFastDivMax: the product
+// is at least n / d, so an exact quotient stays whole, and it exceeds n / d by less than
+// (n + d) 2^-23 / d, which stays below the distance 1 / d to the next integer.
+constexpr int32_t kFastDivMax = 1 << 21;
+float rcp_up(int32_t d) {
+  float r = 1.0f / float(d);
+  if (double(r) * d < 1.0) r = std::nextafter(r, 2.0f);
+  return r;
+}
+__device__ __forceinline__ int idiv(int n, float r) { return int(float(n) * r); }
+
+// Wave-uniform indices use a multiply-high on the scalar unit (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994, the round-up multiplier of
+// N + 1 bits): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// floor(n / d) = (mulhi(n, m) + n) >> l for 0 <= n < 2^31 (the sum cannot wrap there).
+struct UDiv {
+  uint32_t m, l;
+};
+UDiv make_udiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  return UDiv{uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1), l};
+}
+__device__ __forceinline__ int udiv(int n, UDiv v) {
+  return int((__umulhi(uint32_t(n), v.m) + uint32_t(n)) >> v.l);
+}
+
 struct MfmaArgs {
   AttnArgs a;
   int32_t group;     // Hq / Hkv
@@ -102,6 +134,8 @@ struct MfmaArgs {
   int32_t xcd_map;   // keep the query blocks of one (unit, split) on one XCD
   int64_t o_offset;  // byte offset of the partial O in the workspace
   double log2_base;  // log2 of the RoPE base: frequency i is 2^(-(2i/d) log2 base)
+  float rcp_group;               // rcp_up(group)
+  UDiv div_qblocks, div_splits, div_hkv;  // make_udiv() of the divisors
 };
 
 struct MergeArgs {
@@ -110,7 +144,10 @@ struct MergeArgs {
   void* out;
   const int32_t* status;
   int32_t Hq, Hkv, N, group, rows, qrows, qblocks, splits;
+  float rcp_group;  // rcp_up(group)
+  UDiv div_hkv;     // make_udiv(Hkv)
 };
+
 
 struct Plan {
   int32_t units, group, rows, n_kp, qrows, qblocks, splits;
@@ -276,17 +313,13 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int kp = wave % n_kp, rb = wave / n_kp;  // key phase, 32-row block
 
   // ---- this workgroup's (sequence, kv head, split, query block)
-  int grp, qb;
-  if (p.xcd_map) {
-    const int slot = blockIdx.x >> 3;
-    grp = int(blockIdx.x & 7) + 8 * (slot / p.qblocks);
-    qb = slot % p.qblocks;
-  } else {
-    grp = blockIdx.x / p.qblocks;
-    qb = blockIdx.x % p.qblocks;
-  }
-  const int unit = grp / p.splits, split = grp % p.splits;
-  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  // (selected, not branched on, so that the kernel arguments arrive in one round trip)
+  const int bx = blockIdx.x, bq = p.xcd_map ? bx >> 3 : bx;
+  const int sq = udiv(bq, p.div_qblocks);
+  const int grp = p.xcd_map ? (bx & 7) + 8 * sq : sq;
+  const int qb = bq - sq * p.qblocks;
+  const int unit = udiv(grp, p.div_splits), split = grp - unit * p.splits;
+  const int b = udiv(unit, p.div_hkv), kvh = unit - b * a.Hkv;
   const int N = a.N;
   const int n_stg = (N + kTile - 1) / kTile;
 
@@ -303,8 +336,9 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int row0 = qb * p.qrows + rb * kRowsWave;
   const int rq = row0 + l32;
   const bool live = rq < p.rows;
-  const int u_q = live ? rq / p.group : 0;
-  const int h_q = kvh * p.group + (live ? rq % p.group : 0);
+  const int uq0 = idiv(rq, p.rcp_group);
+  const int u_q = live ? uq0 : 0;
+  const int h_q = kvh * p.group + (live ? rq - __mul24(uq0, p.group) : 0);
   uint32_t st_word = load_b32(a.status);  // written by earlier kernels only: a plain load
   // The query rows of the workgroup are fetched once (not once per key phase) by direct
   // loads into the two ring slots that no stage occupies before the first steady step:
@@ -322,10 +356,12 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       const int rt = 16 * kp + 4 * h + (lane >> 4);
       const int rr = row0 + rt;
       const bool lv = rr < p.rows;
-      const int u = lv ? rr / p.group : 0;
-      const int hh = kvh * p.group + (lv ? rr % p.group : 0);
+      const int u0 = idiv(rr, p.rcp_group);
+      const int u = lv ? u0 : 0;
+      const int hh = kvh * p.group + (lv ? rr - __mul24(u0, p.group) : 0);
       const int c = (lane & 15) ^ swz_key(rt);
-      dma16(qseq, uint32_t(((u * a.Hq + hh) * kDH + 8 * src_chunk<kDH>(c)) * 2), dst + 1024 * h);
+      // (24-bit products: rows and heads are far below 2^24)
+      dma16(qseq, uint32_t(((__mul24(u, a.Hq) + hh) * kDH + 8 * src_chunk<kDH>(c)) * 2), dst + 1024 * h);
     }
   }
   uint32_t dep_q_w = load_b32(a.depth + u_q);
@@ -347,7 +383,9 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // general path) count twice, so the last split, which holds them, gets fewer stages.
   const int n_heavy = n_stages - (P / kTile) / n_kp;
   auto bound = [&](int k) __attribute__((always_inline)) {
-    return k == p.splits ? n_stages : min(n_stages, int(int64_t(k) * (n_stages + n_heavy) / p.splits));
+    const int64_t num = int64_t(k) * (n_stages + n_heavy);
+    const int q = num <= INT32_MAX ? udiv(int(num), p.div_splits) : int(num / p.splits);
+    return k == p.splits ? n_stages : min(n_stages, q);
   };
   const int s_lo = bound(split);
   const int n_st = bound(split + 1) - s_lo;
@@ -1120,9 +1158,9 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
   }
   if (failed) return;
   const float inv = 1.0f / L;
-  const int b = unit / p.Hkv, kvh = unit - b * p.Hkv;
-  const uint32_t u = uint32_t(row) / uint32_t(p.group);
-  const int h = kvh * p.group + (row - int(u) * p.group);
+  const int b = udiv(unit, p.div_hkv), kvh = unit - b * p.Hkv;
+  const int u = idiv(row, p.rcp_group);
+  const int h = kvh * p.group + (row - u * p.group);
   bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kDH + 8 * d8;
   bf16x8 ov;
 #pragma unroll
@@ -1132,9 +1170,14 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
 
 }  // namespace
 
-bool mfma_path_applies(medusa_dtype dt, int32_t Hq, int32_t, int32_t d_h, int32_t N) {
+bool mfma_path_applies(medusa_dtype dt, int32_t Hq, int32_t Hkv, int32_t d_h, int32_t N) {
+  if (dt != MEDUSA_BF16 || (d_h != kD && d_h != kD / 2)) return false;
   // one sequence's query rows are addressed with 32-bit byte offsets
-  return dt == MEDUSA_BF16 && (d_h == kD || d_h == kD / 2) && int64_t(N) * Hq * d_h * 2 <= int64_t(UINT32_MAX);
+  if (int64_t(N) * Hq * d_h * 2 > int64_t(UINT32_MAX)) return false;
+  // query rows (those of the last query block included) stay in idiv()'s range
+  const int64_t qrows = kRowsWave * kWaves / kKeyPhases;
+  const int64_t rows = int64_t(N) * (Hq / Hkv), qblocks = (rows + qrows - 1) / qrows;
+  return qblocks * qrows < kFastDivMax;
 }
 
 size_t attn_workspace_bytes(medusa_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d_h,
@@ -1158,6 +1201,10 @@ medusa_status run_mfma(AttnArgs& a, int32_t d_h, hipStream_t stream, void* ev_st
   p.o_offset = int64_t(plan.o_offset);
   // the layout's frequency j is base^(-2 j / d_h): pair i = j of the head's RoPE
   p.log2_base = std::log2(a.rope_base) * (double(kD) / d_h);
+  p.rcp_group = rcp_up(plan.group);
+  p.div_qblocks = make_udiv(uint32_t(plan.qblocks));
+  p.div_splits = make_udiv(uint32_t(plan.splits));
+  p.div_hkv = make_udiv(uint32_t(a.Hkv));
   const unsigned grid = unsigned(int64_t(plan.units) * plan.splits * plan.qblocks);
   const bool full = d_h == kD;
   const void* attn = full ? reinterpret_cast<const void*>(&tree_attn_mfma_kernel<kD>)
@@ -1178,6 +1225,8 @@ medusa_status run_mfma(AttnArgs& a, int32_t d_h, hipStream_t stream, void* ev_st
   m.qrows = plan.qrows;
   m.qblocks = plan.qblocks;
   m.splits = plan.splits;
+  m.rcp_group = rcp_up(plan.group);
+  m.div_hkv = make_udiv(uint32_t(a.Hkv));
   const void* merge =
       full ? (plan.splits <= 4 ? reinterpret_cast<const void*>(&tree_attn_merge_kernel<4, kD>)
                                : reinterpret_cast<const void*>(&tree_attn_merge_kernel<8, kD>))

@@ -67,6 +67,13 @@ EDGE = {
     "mfma_d64_chain": (dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=8, Hkv=2, d=64,
                                            tree="cartesian", branching=(1,) * 20, num_heads=20, topk=1),
                        [300, 1000]),
+    # matrix-core path with GQA groups that are not powers of two (query rows split into
+    # node and head by a run-time divisor): 3 over two query blocks, 5 with d_h = 64 over
+    # three, 7 over four with a single sequence
+    "mfma_group3": (dataclasses.replace(workloads.WORKLOADS["batched"], B=3, Hq=6, Hkv=2), [900, 2500, 17]),
+    "mfma_group5_d64": (dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=10, Hkv=2, d=64),
+                        [1234, 640]),
+    "mfma_group7": (dataclasses.replace(workloads.WORKLOADS["batched"], B=1, Hq=7, Hkv=1), [3000]),
     # a chain: ordinary causal attention over prefix + path
     "chain_f32": (dataclasses.replace(workloads.WORKLOADS["tiny"], Hq=2, Hkv=1, d=128,
                                       branching=(1, 1, 1, 1), num_heads=4, topk=1), [65]),
