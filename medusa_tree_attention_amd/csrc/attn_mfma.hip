@@ -340,28 +340,19 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   const int u_q = live ? uq0 : 0;
   const int h_q = kvh * p.group + (live ? rq - __mul24(uq0, p.group) : 0);
   uint32_t st_word = load_b32(a.status);  // written by earlier kernels only: a plain load
-  // The query rows of the workgroup are fetched once (not once per key phase) by direct
-  // loads into the two ring slots that no stage occupies before the first steady step:
-  // wavefront (rb, kp) fetches rows 16 kp .. 16 kp + 15 of row block rb, four whole
-  // 256-byte rows per instruction, swizzled like the key tiles (lane l lands at chunk l % 16
-  // of its row and fetches logical chunk (l % 16) ^ key(row)).  Each wavefront reads its
-  // 32 rows back in operand order after the set-up barrier.  Rows past the block repeat
-  // the first row of the sequence and are zeroed after the read.
-  unsigned char* const q_stage = s_ring[kRing - 2] + rb * (kRowsWave * kD * 2);
+  // The query inputs of the rotation below, straight into registers with the other set-up
+  // loads: of this lane's row, the dim pairs its wavefront rotates (s = 2 kp + t, t < 2:
+  // layout chunk 2 s + half and its partner 2 s + 8 + half), 16 bytes each.  Rows past the
+  // block read the sequence's first row and are zeroed at the rotation, as are the padding
+  // chunks of a 64-wide head.
+  u32x4 qin[2][2];
   {
-    const bf16* qseq = static_cast<const bf16*>(a.q) + int64_t(b) * N * a.Hq * kDH;
-    const uint32_t dst = lds_addr(q_stage) + 256 * 16 * kp;
+    const bf16* qrow = static_cast<const bf16*>(a.q) + ((int64_t(b) * N + u_q) * a.Hq + h_q) * kDH;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int rt = 16 * kp + 4 * h + (lane >> 4);
-      const int rr = row0 + rt;
-      const bool lv = rr < p.rows;
-      const int u0 = idiv(rr, p.rcp_group);
-      const int u = lv ? u0 : 0;
-      const int hh = kvh * p.group + (lv ? rr - __mul24(u0, p.group) : 0);
-      const int c = (lane & 15) ^ swz_key(rt);
-      // (24-bit products: rows and heads are far below 2^24)
-      dma16(qseq, uint32_t(((__mul24(u, a.Hq) + hh) * kDH + 8 * src_chunk<kDH>(c)) * 2), dst + 1024 * h);
+    for (int t = 0; t < 2; ++t) {
+      const int c = 2 * (2 * kp + t) + half;
+      qin[t][0] = load_b128(qrow + 8 * src_chunk<kDH>(c));
+      qin[t][1] = load_b128(qrow + 8 * src_chunk<kDH>(c + 8));
     }
   }
   uint32_t dep_q_w = load_b32(a.depth + u_q);
@@ -464,13 +455,15 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       wait_vm(n);
   };
 
-  // The first stage's tile loads need only P (a scalar load): issue them now, behind the
-  // set-up loads, unless P is out of range (checked for every sequence below, which then
-  // raises the error).  The rest of the ring is filled once they have landed, so that the
-  // first stage does not share the start-up burst with the next ones.
+  // The tile loads of the first two stages need only P (a scalar load): issue them now,
+  // behind the set-up loads, unless P is out of range (checked for every sequence below,
+  // which then raises the error).  Their ring slots hold nothing else during the set-up;
+  // the rest of the ring is filled once every wavefront has read its query operands from
+  // the slots of stages 2 and 3.
   const bool ring_ok = P >= 0 && P <= a.S_max - N && n_st > 0;
-  if (ring_ok) issue_stage(0);
-  const int n_ring_loads = ring_ok ? 2 * kDmaOps * (tile_end(0) - tile_start(0)) : 0;
+  const int early = ring_ok ? min(2, n_st) : 0;  // stages issued now
+  for (int i = 0; i < early; ++i) issue_stage(i);
+  const int n_ring_loads = early > 0 ? 2 * kDmaOps * (tile_end(early - 1) - tile_start(0)) : 0;
 
   // ---- RoPE phases (cos, sin) of positions P + d: the angle is formed and reduced modulo
   // 2 pi in binary64, then evaluated in fp32.  The depths below kEarlyDepth need only P and
@@ -478,15 +471,10 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // per thread: (d, tid % 64) with d = tid / 64.  Deeper phases, which few trees need, are
   // formed once the node depths are known.
   static_assert(kThreads == kEarlyDepth * (kD / 2), "one early phase entry per thread");
-  // the query staging (one 8 KiB block per row block) fits the two ring slots that the
-  // stages in flight before the first steady step (0 .. S-2) leave free
-  static_assert((kWaves / kKeyPhases) * kRowsWave * kD * 2 <= 2 * kTileBytes &&
-                    (kRing / kKeyPhases - 1) * kKeyPhases <= kRing - 2,
-                "query staging overlaps the ring");
   // the rotated query operands (16 per row block, 16 bytes per lane) fit the slots of stages
-  // 1 .. S-2, which are issued only once every wavefront has read them
-  static_assert((kWaves / kKeyPhases) * 16 * 64 * 16 <= (kRing - 2 - kKeyPhases) * kTileBytes,
-                "query operands overlap the staging or the first stage");
+  // 2 and 3, which are issued only once every wavefront has read them
+  static_assert(kRing / kKeyPhases == 4 && (kWaves / kKeyPhases) * 16 * 64 * 16 <= 2 * kKeyPhases * kTileBytes,
+                "query operands overlap the first two stages");
   const double theta = exp2(-double(tid % (kD / 2)) * (2.0 / kD) * p.log2_base);
   auto phase = [&](int d) __attribute__((always_inline)) {
     const double x = double(P + d) * theta;
@@ -500,6 +488,11 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // the set-up loads are older than the ring's tile loads, which may stay in flight
   wait_vm(n_ring_loads);
   pin(st_word);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    pin(qin[t][0]);
+    pin(qin[t][1]);
+  }
   pin(dep_q_w);
   pin(dep0_w);
   pin(P_lane_w);
@@ -559,29 +552,42 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // lane holds query column l32, dims 16 s + 8 half + e (e < 8).  The two wavefronts of a row
   // block (its two key phases) share the rotation: wavefront kp rotates the dim pairs of
   // s = 2 kp, 2 kp + 1 (dims 16 s.. and their partners 64 + 16 s..) and leaves its hi and lo
-  // operands in LDS, in the ring slots of stages 1 and 2 (issued only after the barrier
-  // below); after the barrier each wavefront reads all sixteen of its row block's operands.
+  // operands in LDS, in the ring slots of stages 2 and 3 (issued only after the barrier
+  // that follows the operand reads); after the barrier below each wavefront reads all
+  // sixteen of its row block's operands.
   const float qscale = kLog2e / sqrtf(float(kDH));
-  unsigned char* const q_ops = s_ring[kKeyPhases] + rb * (16 * 64 * 16);  // [operand][lane] x 16 B
+  unsigned char* const q_ops = s_ring[2 * kKeyPhases] + rb * (16 * 64 * 16);  // [operand][lane] x 16 B
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int s = 2 * kp + t;
     const bool real = live && real_chunk<kDH>(2 * s + half);  // its partner chunk 2 s + 8 + half is alike
-    const bf16x8 lo = __builtin_bit_cast(
-        bf16x8, real ? *reinterpret_cast<const u32x4*>(q_stage + swz(l32, 2 * s + half)) : u32x4{0u, 0u, 0u, 0u});
-    const bf16x8 hi = __builtin_bit_cast(
-        bf16x8, real ? *reinterpret_cast<const u32x4*>(q_stage + swz(l32, 2 * s + 8 + half)) : u32x4{0u, 0u, 0u, 0u});
+    const bf16x8 lo = __builtin_bit_cast(bf16x8, real ? qin[t][0] : u32x4{0u, 0u, 0u, 0u});
+    const bf16x8 hi = __builtin_bit_cast(bf16x8, real ? qin[t][1] : u32x4{0u, 0u, 0u, 0u});
     bf16x8 h1, h2, l1, l2;
+    // element pairs, so that each bf16 rounding is one packed conversion of two values
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float2 cs = s_cs[dep_q][16 * s + 8 * half + e];
-      const float x1 = float(lo[e]), x2 = float(hi[e]);
-      const float r1 = (x1 * cs.x - x2 * cs.y) * qscale;
-      const float r2 = (x2 * cs.x + x1 * cs.y) * qscale;
-      h1[e] = static_cast<bf16>(r1);
-      h2[e] = static_cast<bf16>(r2);
-      l1[e] = static_cast<bf16>(r1 - float(h1[e]));
-      l2[e] = static_cast<bf16>(r2 - float(h2[e]));
+    for (int e = 0; e < 8; e += 2) {
+      f32x2 r1, r2;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float2 cs = s_cs[dep_q][16 * s + 8 * half + e + k];
+        const float x1 = float(lo[e + k]), x2 = float(hi[e + k]);
+        r1[k] = (x1 * cs.x - x2 * cs.y) * qscale;
+        r2[k] = (x2 * cs.x + x1 * cs.y) * qscale;
+      }
+      const bf16x2 a1 = __builtin_convertvector(r1, bf16x2), a2 = __builtin_convertvector(r2, bf16x2);
+      const bf16x2 b1 = __builtin_convertvector(r1 - __builtin_convertvector(a1, f32x2), bf16x2);
+      const bf16x2 b2 = __builtin_convertvector(r2 - __builtin_convertvector(a2, f32x2), bf16x2);
+      h1[e] = a1[0];
+      h1[e + 1] = a1[1];
+      h2[e] = a2[0];
+      h2[e + 1] = a2[1];
+      l1[e] = b1[0];
+      l1[e + 1] = b1[1];
+      l2[e] = b2[0];
+      l2[e + 1] = b2[1];
     }
     // operand o: hi s = o, lo s = 8 + o
     *reinterpret_cast<u32x4*>(q_ops + (s * 64 + lane) * 16) = __builtin_bit_cast(u32x4, h1);
@@ -829,10 +835,10 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   uint32_t b_cur = 0u, b_nxt = 0u;
   const int first = min(S - 1, n_st);  // stages in flight ahead of the loop
   if (n_st > 0) {
-    wait_stage(0, 0);
+    wait_stage(0, early - 1);
     fix_stage(0);
     __syncthreads();  // stage 0 visible; every wavefront has read its query operands
-    for (int i = 1; i < first; ++i) issue_stage(i);  // fill the rest of the ring but one slot
+    for (int i = early; i < first; ++i) issue_stage(i);  // fill the rest of the ring but one slot
     prep(0, s_cur, b_cur);
   }
 
@@ -962,11 +968,18 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   {
     float* give = reinterpret_cast<float*>(&s_ring[0][0]) + (2 * rb + kp) * (32 * 64 + 2 * 64);
     const float* take = reinterpret_cast<const float*>(&s_ring[0][0]) + (2 * rb + (kp ^ 1)) * (32 * 64 + 2 * 64);
+    // (16-byte pieces: four values of a lane side by side, so that the exchange takes 8 LDS
+    // writes and reads per lane rather than 32)
+    float4* const give4 = reinterpret_cast<float4*>(give);
+    const float4* const take4 = reinterpret_cast<const float4*>(take);
     auto hand_over = [&](auto first) __attribute__((always_inline)) {  // blocks first, first + 1
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) give[(j * 16 + e) * 64 + lane] = oacc[decltype(first)::value + j][e];
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& v = oacc[decltype(first)::value + j];
+          give4[(j * 4 + q) * 64 + lane] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
     };
     if (kp == 0)
       hand_over(std::integral_constant<int, 2>{});
@@ -985,9 +998,14 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          oacc[decltype(first)::value + j][e] =
-              w0 * oacc[decltype(first)::value + j][e] + w1 * take[(j * 16 + e) * 64 + lane];
+        for (int q = 0; q < 4; ++q) {
+          const float4 t = take4[(j * 4 + q) * 64 + lane];
+          f32x16& v = oacc[decltype(first)::value + j];
+          v[4 * q] = w0 * v[4 * q] + w1 * t.x;
+          v[4 * q + 1] = w0 * v[4 * q + 1] + w1 * t.y;
+          v[4 * q + 2] = w0 * v[4 * q + 2] + w1 * t.z;
+          v[4 * q + 3] = w0 * v[4 * q + 3] + w1 * t.w;
+        }
     };
     if (kp == 0)
       combine(std::integral_constant<int, 0>{});
