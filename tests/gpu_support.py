@@ -84,30 +84,35 @@ class AttnRun:
         err = max(float(np.abs(got[b, u, h] - out_ref[b, u, h]).max()) for b, u, h in rows)
         kc, vc = host(self.kc), host(self.vc)
         N = self.x["N"]
-        d = self.w.d
         staged_err = 0.0
         for b in range(self.w.B):
             P = int(self.x["prefix_len"][b])
             gk, gv = kc[b, :, P:P + N], vc[b, :, P:P + N]
-            exact_k = sk[b]
-            # |x1| + |x2| of the rotate-half pair each staged element is formed from
-            kn = np.abs(self.x["k_new"][b].transpose(1, 0, 2).astype(np.float64))
-            pair = kn + np.roll(kn, d // 2, axis=-1)
-            if self.w.dtype == "bf16":
-                # rotated in fp32 (the phase angle is reduced in binary64 and rounded to fp32,
-                # about pi 2^-24 rad, then sincosf; with two products and a sum the value is
-                # within 2^-20 (|x1| + |x2|)), then rounded once to bf16 (unit roundoff 2^-8)
-                bound = 2.0 ** -8 * np.abs(exact_k) + 2.0 ** -20 * pair
-            else:
-                # rotated in binary64 and rounded once to fp32 (unit roundoff 2^-24); each
-                # side's binary64 angle at positions below ~8300 is within 3e-12 rad
-                bound = 2.0 ** -24 * np.abs(exact_k) + 1e-11 * pair
-            staged_err = max(staged_err, float((np.abs(gk - exact_k) / bound).max()))
+            staged_err = max(staged_err, staged_k_ratio(self.w, self.x, b, gk, sk[b], np.arange(N)))
             assert np.array_equal(gv, sv[b].astype(np.float32)), "staged V rows differ"
             # rows outside the staged block are untouched
             assert np.array_equal(kc[b, :, :P], self.x["k_cache"][b, :, :P])
             assert np.array_equal(kc[b, :, P + N:], self.x["k_cache"][b, :, P + N:])
         return err, staged_err
+
+
+def staged_k_ratio(w, x, b, got, exact, nodes):
+    """Largest error of staged key rows (of the given nodes, [Hkv][len(nodes)][d]) against the
+    oracle's binary64 rotation, as a fraction of the bound the kernel's arithmetic allows."""
+    d = w.d
+    # |x1| + |x2| of the rotate-half pair each staged element is formed from
+    kn = np.abs(x["k_new"][b].transpose(1, 0, 2).astype(np.float64))[:, nodes]
+    pair = kn + np.roll(kn, d // 2, axis=-1)
+    if w.dtype == "bf16":
+        # rotated in fp32 (the phase angle is reduced in binary64 and rounded to fp32, about
+        # pi 2^-24 rad, then sincosf; with two products and a sum the value is within
+        # 2^-20 (|x1| + |x2|)), then rounded once to bf16 (unit roundoff 2^-8)
+        bound = 2.0 ** -8 * np.abs(exact) + 2.0 ** -20 * pair
+    else:
+        # rotated in binary64 and rounded once to fp32 (unit roundoff 2^-24); each side's
+        # binary64 angle at positions below ~8300 is within 3e-12 rad
+        bound = 2.0 ** -24 * np.abs(exact) + 1e-11 * pair
+    return float((np.abs(got - exact) / bound).max())
 
 
 def sample_rows(w, N, n, seed=0, must=()):

@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from gpu_support import TOL, AttnRun, announce, compile_both, dev, host, oracle_accept, sample_rows  # noqa: E402
+from gpu_support import (TOL, AttnRun, announce, compile_both, dev, host, oracle_accept,  # noqa: E402
+                         sample_rows, staged_k_ratio)
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))
@@ -68,3 +69,14 @@ def test_round(name):
                            x["prefix_len"], x["N"])
     assert np.array_equal(prefix.cpu().numpy(), new_len)
     assert np.array_equal(host(att.kc), caches[0]) and np.array_equal(host(att.vc), caches[1])
+
+    # end to end against the oracle: committed row P + j of sequence b holds node r[j] of the
+    # winning path -- its staged key within one rounding of the oracle's binary64 rotation,
+    # its value exactly
+    _, sk, sv = att.oracle(rows[:1])
+    kc_now, vc_now = host(att.kc), host(att.vc)
+    for b in range(w.B):
+        P, G = int(x["prefix_len"][b]), int(ref["accept_len"][b]) + 1
+        path = ora["retrieve"][ref["best_path"][b]][:G]
+        assert staged_k_ratio(w, x, b, kc_now[b, :, P:P + G], sk[b][:, path], path) <= 1.0
+        assert np.array_equal(vc_now[b, :, P:P + G], sv[b][:, path].astype(np.float32))
