@@ -782,177 +782,192 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
       }
   };
 
-  // prep: this wavefront's tile of stage i -- visibility bits and scores
-  auto prep = [&](int i, f32x16& s, uint32_t& bits) __attribute__((always_inline)) {
-    const int t = tile_start(i) + kp;
-    if (t < T) {
-      bits = tile_bits(t);
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        bf16x8 kop[4];
-        read_k(tbuf(i, kp), kh, kop);
-        qk(kh, kop, s);
-      }
-    }
-  };
-  // consume: masking, softmax and PV of this wavefront's tile of stage i
-  auto consume = [&](int i, f32x16& s, uint32_t bits) __attribute__((always_inline)) {
-    const int t = tile_start(i) + kp;
-    if (t >= T) return;
-    if (t >= n_pre - 1) {  // the last prefix tile or a staged tile
-      // element e holds key 8 (e / 4) + 4 half + e % 4; shifting by 4 half first leaves
-      // compile-time bit positions
-      const uint32_t bh = bits >> (4 * half);
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (!((bh >> (8 * (e >> 2) + (e & 3))) & 1u)) s[e] = -INFINITY;
-    }
-    const float m_use = update_max(s);
-    bf16x8 pop[2];
-    probs(s, m_use, pop);
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh) {
-      bf16x8 vop[2][2];
-      read_v(tbuf(i, kp), dh, vop);
-      pv(dh, vop, pop);
-    }
-  };
-  // one step: publish stage i+1 and refill the slot of stage i-1, form the scores of
-  // stage i+1 on the matrix core, then finish stage i
-  auto step = [&](int i, f32x16& s_cur, uint32_t& b_cur, f32x16& s_nxt, uint32_t& b_nxt)
-      __attribute__((always_inline)) {
-    if (i + 1 < n_st) {
-      wait_stage(i + 1, min(i + S - 2, n_st - 1));
-      fix_stage(i + 1);
-      __syncthreads();  // stage i+1 visible; every wavefront is done with stage i-1
-      if (i + S - 1 < n_st) issue_stage(i + S - 1);
-      prep(i + 1, s_nxt, b_nxt);
-    }
-    consume(i, s_cur, b_cur);
-  };
-
-  f32x16 s_cur, s_nxt;
-  uint32_t b_cur = 0u, b_nxt = 0u;
-  const int first = min(S - 1, n_st);  // stages in flight ahead of the loop
-  if (n_st > 0) {
-    wait_stage(0, early - 1);
-    fix_stage(0);
-    __syncthreads();  // stage 0 visible; every wavefront has read its query operands
-    for (int i = early; i < first; ++i) issue_stage(i);  // fill the rest of the ring but one slot
-    prep(0, s_cur, b_cur);
-  }
-
-  // Steady state.  Step i is steady when every tile it touches -- those of stages i and
-  // i+1 and those of stage i+S-1, which it issues -- is a full prefix tile (index below
-  // P / kTile) and the ring is full.  Such steps need no tile classification, masks,
-  // staged-row fixes or variable waits, and their load addresses advance by a fixed
-  // stride, so they run as a separate loop with as few instructions as possible.  The
-  // remaining steps (the ring's drain, partial and staged tiles) take the general path.
-  // stages of this split whose tiles are all full prefix tiles; a step over two of them
-  // needs no masks, and while the stage it issues is one of them its loads advance by a
-  // fixed stride with a fixed wait; the ring's drain issues through issue_stage()
-  const int n_full = max(0, min(n_st, (P / kTile) / n_kp - s_lo));
-  const int fast_end = max(0, n_full - 1);
-  const int hot_end = max(0, n_full - S + 1);
-  int i = 0;
-  if (fast_end > 0) {
-    // The running maximum is checked at the end of each step, on the scores just formed,
-    // and moved (rarely) before they are used.
-    update_max(s_cur);
-    f32x16 zero;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) zero[e] = 0.f;
-    // global addresses of the tiles of stage S-1 (issued by step 0); lane offsets in poff[]
-    const bf16* kq = kc + int64_t((s_lo + S - 1) * n_kp) * kTile * kDH;
-    const bf16* vq = vc + int64_t((s_lo + S - 1) * n_kp) * kTile * kDH;
-    const uint32_t ring0 = lds_addr(&s_ring[0][0]) + 256 * kDmaRows * wave;
-    auto steady = [&](int j, f32x16& sc, f32x16& sn, auto fixed) __attribute__((always_inline)) {
-      if constexpr (decltype(fixed)::value) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteadyWait) : "memory");
-        __syncthreads();  // stage j+1 visible; every wavefront is done with stage j-1
-        const uint32_t dst = ring0 + uint32_t(((j + S - 1) & (S - 1)) * n_kp * kTileBytes);
-#pragma unroll
-        for (int k = 0; k < n_kp; ++k)
-#pragma unroll
-          for (int h = 0; h < kDmaOps; ++h) {
-            dma16(kq + k * kTile * kDH, poff[h], dst + k * kTileBytes + 1024 * h);
-            dma16(vq + k * kTile * kDH, poff[h], dst + k * kTileBytes + 8192 + 1024 * h);
-          }
-        kq += n_kp * kTile * kDH;
-        vq += n_kp * kTile * kDH;
-      } else {
-        wait_stage(j + 1, min(j + S - 2, n_st - 1));
-        __syncthreads();
-        if (j + S - 1 < n_st) issue_stage(j + S - 1);
-      }
-      const unsigned char* tn = s_ring[((j + 1) & (S - 1)) * n_kp + kp];
-      const unsigned char* tc = s_ring[(j & (S - 1)) * n_kp + kp];
-      // the operand reads of the step: the first half of the K operands and every V operand
-      // up front, the second half of the K operands once the first half is in use (the
-      // query rows, carried as a hi/lo pair, leave no room for all of them at once)
-      bf16x8 kop[4], vop[2][2][2];
-      read_k(tn, 0, kop);
-      read_v(tc, 0, vop[0]);
-      read_v(tc, 1, vop[1]);
-      // probabilities of tile j against the running maximum
-      bf16x8 pop[2];
-      probs(sc, m_run, pop);
-      // scores of tile j+1
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        if (kh == 1) read_k(tn, 1, kop);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj], qhi[4 * kh + jj], kh == 0 && jj == 0 ? zero : sn, 0, 0, 0);
-          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj], qlo[4 * kh + jj], sn, 0, 0, 0);
+  // The key loop, instantiated twice: a row block past the unit's last query row (the upper
+  // half of a 128-row block when a unit has 64 rows, e.g. one query head per kv head) still
+  // loads its share of every tile, fixes its staged rows and keeps every barrier, but forms
+  // no scores and no output.
+  auto key_loop = [&](auto dead_tag) __attribute__((always_inline)) {
+    constexpr bool kDead = decltype(dead_tag)::value;
+    // prep: this wavefront's tile of stage i -- visibility bits and scores
+    auto prep = [&](int i, f32x16& s, uint32_t& bits) __attribute__((always_inline)) {
+      if constexpr (kDead) return;
+      const int t = tile_start(i) + kp;
+      if (t < T) {
+        bits = tile_bits(t);
+  #pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          bf16x8 kop[4];
+          read_k(tbuf(i, kp), kh, kop);
+          qk(kh, kop, s);
         }
       }
-      pv(0, vop[0], pop);
-      pv(1, vop[1], pop);
-      // maximum of tile j+1; the reference moves when it exceeds the slack
-      float x0 = max3f(sn[0], sn[1], sn[2]), x1 = max3f(sn[3], sn[4], sn[5]);
-      float x2 = max3f(sn[6], sn[7], sn[8]), x3 = max3f(sn[9], sn[10], sn[11]);
-      float x4 = max3f(sn[12], sn[13], sn[14]);
-      x0 = max3f(x0, x1, x2);
-      x3 = max3f(x3, x4, sn[15]);
-      x0 = max2f(x0, x3);
-      float y0, y1;
-      halves(x0, y0, y1);
-      const float tmax = max2f(y0, y1);
-      const bool grow = tmax > m_run + kRescaleSlack;
-      if (__ballot(grow)) {
-        const float m_new = grow ? tmax : m_run;
-        const float corr = exp2_fast(m_run - m_new);
-        l_run *= corr;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
-        m_run = m_new;
+    };
+    // consume: masking, softmax and PV of this wavefront's tile of stage i
+    auto consume = [&](int i, f32x16& s, uint32_t bits) __attribute__((always_inline)) {
+      if constexpr (kDead) return;
+      const int t = tile_start(i) + kp;
+      if (t >= T) return;
+      if (t >= n_pre - 1) {  // the last prefix tile or a staged tile
+        // element e holds key 8 (e / 4) + 4 half + e % 4; shifting by 4 half first leaves
+        // compile-time bit positions
+        const uint32_t bh = bits >> (4 * half);
+  #pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (!((bh >> (8 * (e >> 2) + (e & 3))) & 1u)) s[e] = -INFINITY;
+      }
+      const float m_use = update_max(s);
+      bf16x8 pop[2];
+      probs(s, m_use, pop);
+  #pragma unroll
+      for (int dh = 0; dh < 2; ++dh) {
+        bf16x8 vop[2][2];
+        read_v(tbuf(i, kp), dh, vop);
+        pv(dh, vop, pop);
       }
     };
-    // unrolled twice so that the two score tiles trade places without copies
-    auto run = [&](int end, auto fixed) __attribute__((always_inline)) {
-      for (; i + 2 <= end; i += 2) {
-        steady(i, s_cur, s_nxt, fixed);
-        steady(i + 1, s_nxt, s_cur, fixed);
+    // one step: publish stage i+1 and refill the slot of stage i-1, form the scores of
+    // stage i+1 on the matrix core, then finish stage i
+    auto step = [&](int i, f32x16& s_cur, uint32_t& b_cur, f32x16& s_nxt, uint32_t& b_nxt)
+        __attribute__((always_inline)) {
+      if (i + 1 < n_st) {
+        wait_stage(i + 1, min(i + S - 2, n_st - 1));
+        fix_stage(i + 1);
+        __syncthreads();  // stage i+1 visible; every wavefront is done with stage i-1
+        if (i + S - 1 < n_st) issue_stage(i + S - 1);
+        prep(i + 1, s_nxt, b_nxt);
       }
-      if (i < end) {
-        steady(i, s_cur, s_nxt, fixed);
-        s_cur = s_nxt;
-        ++i;
-      }
+      consume(i, s_cur, b_cur);
     };
-    run(hot_end, std::true_type{});
-    run(fast_end, std::false_type{});
-    b_cur = 0xffffffffu;  // the current tile is a full prefix tile
-  }
-  // the remaining steps: the end of the ring, partial and staged tiles
-  for (; i < n_st; ++i) {
-    step(i, s_cur, b_cur, s_nxt, b_nxt);
-    s_cur = s_nxt;
-    b_cur = b_nxt;
-  }
+
+    f32x16 s_cur, s_nxt;
+    uint32_t b_cur = 0u, b_nxt = 0u;
+    const int first = min(S - 1, n_st);  // stages in flight ahead of the loop
+    if (n_st > 0) {
+      wait_stage(0, early - 1);
+      fix_stage(0);
+      __syncthreads();  // stage 0 visible; every wavefront has read its query operands
+      for (int i = early; i < first; ++i) issue_stage(i);  // fill the rest of the ring but one slot
+      prep(0, s_cur, b_cur);
+    }
+
+    // Steady state.  Step i is steady when every tile it touches -- those of stages i and
+    // i+1 and those of stage i+S-1, which it issues -- is a full prefix tile (index below
+    // P / kTile) and the ring is full.  Such steps need no tile classification, masks,
+    // staged-row fixes or variable waits, and their load addresses advance by a fixed
+    // stride, so they run as a separate loop with as few instructions as possible.  The
+    // remaining steps (the ring's drain, partial and staged tiles) take the general path.
+    // stages of this split whose tiles are all full prefix tiles; a step over two of them
+    // needs no masks, and while the stage it issues is one of them its loads advance by a
+    // fixed stride with a fixed wait; the ring's drain issues through issue_stage()
+    const int n_full = max(0, min(n_st, (P / kTile) / n_kp - s_lo));
+    const int fast_end = max(0, n_full - 1);
+    const int hot_end = max(0, n_full - S + 1);
+    int i = 0;
+    if (fast_end > 0) {
+      // The running maximum is checked at the end of each step, on the scores just formed,
+      // and moved (rarely) before they are used.
+      if constexpr (!kDead) update_max(s_cur);
+      f32x16 zero;
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+      // global addresses of the tiles of stage S-1 (issued by step 0); lane offsets in poff[]
+      const bf16* kq = kc + int64_t((s_lo + S - 1) * n_kp) * kTile * kDH;
+      const bf16* vq = vc + int64_t((s_lo + S - 1) * n_kp) * kTile * kDH;
+      const uint32_t ring0 = lds_addr(&s_ring[0][0]) + 256 * kDmaRows * wave;
+      auto steady = [&](int j, f32x16& sc, f32x16& sn, auto fixed) __attribute__((always_inline)) {
+        if constexpr (decltype(fixed)::value) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteadyWait) : "memory");
+          __syncthreads();  // stage j+1 visible; every wavefront is done with stage j-1
+          const uint32_t dst = ring0 + uint32_t(((j + S - 1) & (S - 1)) * n_kp * kTileBytes);
+  #pragma unroll
+          for (int k = 0; k < n_kp; ++k)
+  #pragma unroll
+            for (int h = 0; h < kDmaOps; ++h) {
+              dma16(kq + k * kTile * kDH, poff[h], dst + k * kTileBytes + 1024 * h);
+              dma16(vq + k * kTile * kDH, poff[h], dst + k * kTileBytes + 8192 + 1024 * h);
+            }
+          kq += n_kp * kTile * kDH;
+          vq += n_kp * kTile * kDH;
+        } else {
+          wait_stage(j + 1, min(j + S - 2, n_st - 1));
+          __syncthreads();
+          if (j + S - 1 < n_st) issue_stage(j + S - 1);
+        }
+        if constexpr (kDead) return;
+        const unsigned char* tn = s_ring[((j + 1) & (S - 1)) * n_kp + kp];
+        const unsigned char* tc = s_ring[(j & (S - 1)) * n_kp + kp];
+        // the operand reads of the step: the first half of the K operands and every V operand
+        // up front, the second half of the K operands once the first half is in use (the
+        // query rows, carried as a hi/lo pair, leave no room for all of them at once)
+        bf16x8 kop[4], vop[2][2][2];
+        read_k(tn, 0, kop);
+        read_v(tc, 0, vop[0]);
+        read_v(tc, 1, vop[1]);
+        // probabilities of tile j against the running maximum
+        bf16x8 pop[2];
+        probs(sc, m_run, pop);
+        // scores of tile j+1
+  #pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          if (kh == 1) read_k(tn, 1, kop);
+  #pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj], qhi[4 * kh + jj], kh == 0 && jj == 0 ? zero : sn, 0, 0, 0);
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj], qlo[4 * kh + jj], sn, 0, 0, 0);
+          }
+        }
+        pv(0, vop[0], pop);
+        pv(1, vop[1], pop);
+        // maximum of tile j+1; the reference moves when it exceeds the slack
+        float x0 = max3f(sn[0], sn[1], sn[2]), x1 = max3f(sn[3], sn[4], sn[5]);
+        float x2 = max3f(sn[6], sn[7], sn[8]), x3 = max3f(sn[9], sn[10], sn[11]);
+        float x4 = max3f(sn[12], sn[13], sn[14]);
+        x0 = max3f(x0, x1, x2);
+        x3 = max3f(x3, x4, sn[15]);
+        x0 = max2f(x0, x3);
+        float y0, y1;
+        halves(x0, y0, y1);
+        const float tmax = max2f(y0, y1);
+        const bool grow = tmax > m_run + kRescaleSlack;
+        if (__ballot(grow)) {
+          const float m_new = grow ? tmax : m_run;
+          const float corr = exp2_fast(m_run - m_new);
+          l_run *= corr;
+  #pragma unroll
+          for (int db = 0; db < 4; ++db)
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
+          m_run = m_new;
+        }
+      };
+      // unrolled twice so that the two score tiles trade places without copies
+      auto run = [&](int end, auto fixed) __attribute__((always_inline)) {
+        for (; i + 2 <= end; i += 2) {
+          steady(i, s_cur, s_nxt, fixed);
+          steady(i + 1, s_nxt, s_cur, fixed);
+        }
+        if (i < end) {
+          steady(i, s_cur, s_nxt, fixed);
+          s_cur = s_nxt;
+          ++i;
+        }
+      };
+      run(hot_end, std::true_type{});
+      run(fast_end, std::false_type{});
+      b_cur = 0xffffffffu;  // the current tile is a full prefix tile
+    }
+    // the remaining steps: the end of the ring, partial and staged tiles
+    for (; i < n_st; ++i) {
+      step(i, s_cur, b_cur, s_nxt, b_nxt);
+      s_cur = s_nxt;
+      b_cur = b_nxt;
+    }
+
+  };
+  if (row0 >= p.rows)
+    key_loop(std::true_type{});
+  else
+    key_loop(std::false_type{});
 
   // ---- combine the key phases.  The two wavefronts of a row block split the work: wavefront
   // kp keeps the output dims of accumulator blocks 2 kp and 2 kp + 1 and hands its partner
