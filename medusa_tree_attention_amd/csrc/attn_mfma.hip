@@ -43,9 +43,9 @@
 //    sums are taken over the bf16-rounded probabilities (the values P V uses)
 //    with packed bf16 dot products.
 //  * Everything the set-up reads from memory (status, prefix lengths, query
-//    rows, node depths, staged visibility words) is loaded at once, together
-//    with the first stage's tiles, and consumed before the rest of the ring is
-//    filled, so that no compiler-inserted wait drains the tile ring.
+//    inputs, node depths, staged visibility words) is loaded at once, together
+//    with the tiles of the first two stages, and consumed before the rest of the
+//    ring is filled, so that no compiler-inserted wait drains the tile ring.
 //  * Staged keys are rotated to P + depth(u) in LDS by the wavefront that
 //    loaded them, written to cache rows P + u by query block 0, and masked per
 //    lane with the ancestor bitmask.  RoPE phases are reduced modulo 2 pi in
@@ -288,6 +288,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 load_b128(const void* p) {
   u32x4 v;
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+// the same, marked nontemporal (data read once)
+__device__ __forceinline__ u32x4 load_b128_nt(const void* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(v) : "v"(p) : "memory");
   return v;
 }
 __device__ __forceinline__ u32x2 load_b64(const void* p) {
@@ -1112,8 +1118,9 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
 #pragma unroll
     for (int i = 0; i < kRowsWave / kRowsPass; ++i) {
       const int row = i * kRowsPass + lane / kLanesRow, c = lane % kLanesRow;
-      *reinterpret_cast<u32x4*>(oh + row * kHalfBytes + 16 * c) =
-          *reinterpret_cast<const u32x4*>(stg + row * kStgStride + 16 * c);
+      // (nontemporal: the partial is read once, by the merge kernel, mostly on another XCD)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + row * kStgStride + 16 * c),
+                                  reinterpret_cast<u32x4*>(oh + row * kHalfBytes + 16 * c));
     }
   };
   if (kp == 0)
@@ -1152,10 +1159,10 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {  // slots past the last split re-read split 0
       const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
-      mlw[k] = load_b128(p.ml + slot);
+      mlw[k] = load_b128_nt(p.ml + slot);
       // O of (split, half hf, row r): [..][split][hf][qrows][d_h / 2]
       const int64_t sp = grp0 + int64_t(s0 + k < p.splits ? s0 + k : 0);
-      v[k] = load_b128(p.o + ((sp * 2 + hf) * p.qrows + r) * (kDH / 2) + din);
+      v[k] = load_b128_nt(p.o + ((sp * 2 + hf) * p.qrows + r) * (kDH / 2) + din);
     }
     wait_vm(0);
     float4 ml[kGroup];  // (m, l, s0, s1)
