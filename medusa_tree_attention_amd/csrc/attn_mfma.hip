@@ -140,7 +140,7 @@ struct MfmaArgs {
 
 struct MergeArgs {
   const float4* ml;  // [units][qblocks][splits][qrows] (m, l, s0, s1): largest |O / l| per half
-  const int16_t* o;  // [units][qblocks][splits][qrows][D], O / (l s) in 16-bit fixed point
+  const unsigned char* o;  // O / (l s) as 16-bit fixed point, in the attention wavefronts' lane order
   void* out;
   const int32_t* status;
   int32_t Hq, Hkv, N, group, rows, qrows, qblocks, splits;
@@ -1066,23 +1066,19 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
   // within 2^-16 s of each value -- well inside the bf16 rounding of the output (2^-9 of |o|)
   // and half the bytes of fp32 partials, which every split writes and the merge reads back.
   // A split that saw no key of the row stores l = s = 0.
-  // The O part is laid out [unit][query block][split][half][query row][d_h / 2]: the rows of a
-  // wavefront's half are one contiguous run, written through LDS (this wavefront's own slice
-  // of the ring, past the exchange areas) as whole 16-byte pieces rather than 8-byte pieces
-  // scattered over 32 rows.
-  const int64_t slot = ((int64_t(unit) * p.qblocks + qb) * p.splits + split) * p.qrows + rb * kRowsWave + l32;
-  float* rec = reinterpret_cast<float*>(static_cast<float4*>(a.workspace) + slot);
-  constexpr int kHalfBytes = kDH;               // d_h / 2 int16 values per row and half
-  constexpr int kStgStride = kHalfBytes + 8;    // padded: the lanes' 8-byte writes hit distinct banks
-  unsigned char* const stg = &s_ring[0][0] + 73728 + wave * (kRowsWave * kStgStride);
-  static_assert(73728 >= kWaves * (32 * 64 + 2 * 64) * 4 && 73728 + kWaves * kRowsWave * (kD + 8) <= kRing * kTileBytes,
-                "the store staging lies past the exchange areas, inside the ring");
-  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  // The O part is kept in lane order: wavefront (rb, kp) of the workgroup owns d_h / 32 KiB in
+  // which lane L's 16-byte piece i sits at 1024 i + 16 L, so that each store instruction
+  // writes one whole KiB straight from registers (and the merge kernel, one thread per lane
+  // of a wavefront, reads it back the same way).  Row blocks past the unit's last query row
+  // store nothing.
+  if (row0 >= p.rows) return;
+  const int64_t pgrp = (int64_t(unit) * p.qblocks + qb) * p.splits + split;  // (unit, query block, split)
+  float* rec = reinterpret_cast<float*>(static_cast<float4*>(a.workspace) + pgrp * p.qrows + rb * kRowsWave + l32);
+  constexpr int kPieces = kDH / 32;  // 16-byte pieces per lane
+  unsigned char* const dst = static_cast<unsigned char*>(a.workspace) + p.o_offset +
+                             ((pgrp * (p.qrows / kRowsWave) + rb) * 2 + kp) * (kPieces * 1024) + 16 * lane;
   auto store_partial = [&](auto first) __attribute__((always_inline)) {
     constexpr int f = decltype(first)::value;
-    unsigned char* const oh = static_cast<unsigned char*>(a.workspace) + p.o_offset +
-                              ((((int64_t(unit) * p.qblocks + qb) * p.splits + split) * 2 + f / 2) * p.qrows +
-                               rb * kRowsWave) * kHalfBytes;
     float amax = 0.f;  // largest |O| of this lane's dims of the half, then of the row's (two lanes)
 #pragma unroll
     for (int db = f; db < f + 2; ++db) {
@@ -1103,24 +1099,22 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
 #pragma unroll
     for (int db = f; db < f + 2; ++db) {
       if (out_block<kDH>(db) < 0) continue;
+      const f32x16& v = oacc[db];
+      // piece (db - f) 2 + j of a 128-wide head, j of a 64-wide one: dims
+      // 32 db + 8 g + 4 half + 0..3 for g = 2 j and 2 j + 1
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& v = oacc[db];
-        const s16x2 a0 = __builtin_amdgcn_cvt_pknorm_i16(v[4 * g] * k, v[4 * g + 1] * k);
-        const s16x2 a1 = __builtin_amdgcn_cvt_pknorm_i16(v[4 * g + 2] * k, v[4 * g + 3] * k);
-        // dims out_block(db) + 8 g + 4 half .. + 3 of the row, at their place within the half
-        *reinterpret_cast<u32x2*>(stg + l32 * kStgStride + (out_block<kDH>(db) - out_block<kDH>(f) + 8 * g + 4 * half) * 2) =
-            u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)};
+      for (int j = 0; j < 2; ++j) {
+        u32x4 pc;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int g = 2 * j + t;
+          pc[2 * t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(v[4 * g] * k, v[4 * g + 1] * k));
+          pc[2 * t + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(v[4 * g + 2] * k, v[4 * g + 3] * k));
+        }
+        const int i = kDH == kD ? (db - f) * 2 + j : j;
+        // (nontemporal: the partial is read once, by the merge kernel, mostly on another XCD)
+        __builtin_nontemporal_store(pc, reinterpret_cast<u32x4*>(dst + 1024 * i));
       }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's staging is complete
-    constexpr int kLanesRow = kHalfBytes / 16, kRowsPass = 64 / kLanesRow;
-#pragma unroll
-    for (int i = 0; i < kRowsWave / kRowsPass; ++i) {
-      const int row = i * kRowsPass + lane / kLanesRow, c = lane % kLanesRow;
-      // (nontemporal: the partial is read once, by the merge kernel, mostly on another XCD)
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + row * kStgStride + 16 * c),
-                                  reinterpret_cast<u32x4*>(oh + row * kHalfBytes + 16 * c));
     }
   };
   if (kp == 0)
@@ -1129,47 +1123,50 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_mfma_kernel(MfmaArgs p)
     store_partial(std::integral_constant<int, 2>{});
 }
 
-// Merge of the splits: thread (row, 8 dims) combines the splits' partials, weighting split
-// s by l_s 2^(m_s - M).  The splits are visited kGroup at a time (four when there are at
-// most four, else eight) with every load of a group issued before any is used, so that a
-// thread waits for memory once per group rather than once per split.
-// query rows per 256-thread block: d_h / 8 threads per row
-template <int kDH>
-constexpr int merge_rows() { return 256 / (kDH / 8); }
-
-// Grid: x = unit, y = query block, z = chunk of merge_rows() rows of the query block, so that
-// every index comes from the launch coordinates without a division by a run-time value.
+// Merge of the splits, one thread per 16-byte piece of an attention wavefront's partial: in
+// the block for wavefront (rb, kp), thread (ph, L) combines, for query row rb 32 + L % 32 of
+// the query block, the eight dims of piece ph of that wavefront's lane L (layout dims
+// 32 db + 8 g + 4 (L / 32) + 0..3 for g = 2 (ph % 2), 2 (ph % 2) + 1 of block db = 2 kp + ph / 2),
+// weighting split s by l_s 2^(m_s - M).  The splits are visited kGroup at a time (four when
+// there are at most four, else eight) with every load of a group issued before any is used,
+// so that a thread waits for memory once per group rather than once per split.
+// Grid: x = unit, y = query block, z = 2 rb + kp; 64 d_h / 32 threads.  Every index comes from
+// the launch coordinates without a division by a run-time value.
 template <int kGroup, int kDH>
-__global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
+__global__ __launch_bounds__(64 * (kDH / 32)) void tree_attn_merge_kernel(MergeArgs p) {
   const bool failed = round_failed(p.status);  // gates the store only
-  const int d8 = threadIdx.x & (kDH / 8 - 1);
-  const int r = int(blockIdx.z) * merge_rows<kDH>() + int(threadIdx.x) / (kDH / 8);  // row of the query block
-  const int qb = int(blockIdx.y), unit = int(blockIdx.x);
-  const int row = qb * p.qrows + r;
-  if (r >= p.qrows || row >= p.rows) return;
+  const int lane = int(threadIdx.x) & 63, l32 = lane & 31, half = lane >> 5, ph = int(threadIdx.x) >> 6;
+  const int unit = int(blockIdx.x), qb = int(blockIdx.y), rb = int(blockIdx.z) >> 1, kp = int(blockIdx.z) & 1;
+  const int row0 = qb * p.qrows + rb * kRowsWave;  // the wavefront's first query row
+  if (row0 >= p.rows) return;                        // a row block past the last query row
+  constexpr int kPieces = kDH / 32, kPer = 1;  // pieces per lane, per thread
   const int64_t grp0 = (int64_t(unit) * p.qblocks + qb) * p.splits;  // (unit, query block, split 0)
-  const int64_t base = grp0 * p.qrows + r;                             // slot of split 0
-  const int hf = 8 * d8 < kDH / 2 ? 0 : 1, din = 8 * d8 - hf * (kDH / 2);  // half and dim within it
   float M = -INFINITY, L = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[kPer][8];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
   for (int s0 = 0; s0 < p.splits; s0 += kGroup) {
     // issued as inline assembly, every load of the group back to back and then one wait:
     // left to itself the compiler waits for each split's load before it issues the next
-    u32x4 mlw[kGroup], v[kGroup];
+    u32x4 mlw[kGroup], v[kGroup][kPer];
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {  // slots past the last split re-read split 0
-      const int64_t slot = base + int64_t(s0 + k < p.splits ? s0 + k : 0) * p.qrows;
-      mlw[k] = load_b128_nt(p.ml + slot);
-      // O of (split, half hf, row r): [..][split][hf][qrows][d_h / 2]
-      const int64_t sp = grp0 + int64_t(s0 + k < p.splits ? s0 + k : 0);
-      v[k] = load_b128_nt(p.o + ((sp * 2 + hf) * p.qrows + r) * (kDH / 2) + din);
+      const int64_t g = grp0 + (s0 + k < p.splits ? s0 + k : 0);
+      mlw[k] = load_b128_nt(p.ml + g * p.qrows + rb * kRowsWave + l32);
+      const unsigned char* src =
+          p.o + ((g * (p.qrows / kRowsWave) + rb) * 2 + kp) * (kPieces * 1024) + 1024 * (kPer * ph) + 16 * lane;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) v[k][i] = load_b128_nt(src + 1024 * i);
     }
     wait_vm(0);
     float4 ml[kGroup];  // (m, l, s0, s1)
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
       pin(mlw[k]);
-      pin(v[k]);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) pin(v[k][i]);
       ml[k] = make_float4(__uint_as_float(mlw[k][0]), __uint_as_float(mlw[k][1]), __uint_as_float(mlw[k][2]),
                           __uint_as_float(mlw[k][3]));
     }
@@ -1181,32 +1178,61 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs p) {
     const float c = M == -INFINITY ? 0.f : exp2_fast(M - Mg);
     L *= c;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= c;
+    for (int i = 0; i < kPer; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i][e] *= c;
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
       const float wt = (s0 + k < p.splits && ml[k].x != -INFINITY) ? ml[k].y * exp2_fast(ml[k].x - Mg) : 0.f;
       L += wt;
       // weight of one fixed-point step: dims of blocks 0, 1 are relative to s0, the rest to s1
-      const float cw = wt * (8 * d8 < kDH / 2 ? ml[k].z : ml[k].w) * (1.0f / 32767.0f);
+      const float cw = wt * (kp == 0 ? ml[k].z : ml[k].w) * (1.0f / 32767.0f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int32_t q = int32_t(int16_t(v[k][e >> 1] >> (16 * (e & 1))));
-        acc[e] += cw * float(q);
-      }
+      for (int i = 0; i < kPer; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int32_t q = int32_t(int16_t(v[k][i][e >> 1] >> (16 * (e & 1))));
+          acc[i][e] += cw * float(q);
+        }
     }
     M = Mg;
   }
   if (failed) return;
+  // The wavefront's 32 rows x d_h / 2 dims go through LDS (rows padded by 8 bytes, so that the
+  // lanes' 8-byte writes down a column spread over the banks) and leave as whole 16-byte pieces,
+  // d_h / 16 threads per row: every store instruction writes whole row halves rather than 8
+  // bytes on each of 32 rows.
+  constexpr int kHalfDims = kDH / 2, kStride = kHalfDims * 2 + 8, kChunks = kHalfDims / 8;
+  __shared__ __attribute__((aligned(16))) unsigned char tile[kRowsWave * kStride];
   const float inv = 1.0f / L;
-  const int b = udiv(unit, p.div_hkv), kvh = unit - b * p.Hkv;
-  const int u = idiv(row, p.rcp_group);
-  const int h = kvh * p.group + (row - u * p.group);
-  bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kDH + 8 * d8;
-  bf16x8 ov;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ov[e] = static_cast<bf16>(acc[e] * inv);
-  *reinterpret_cast<bf16x8*>(o) = ov;
+  for (int i = 0; i < kPer; ++i) {
+    const int ig = kPer * ph + i;  // the piece of the lane
+    const int db = kDH == kD ? 2 * kp + ig / 2 : 2 * kp;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int g = 2 * (ig & 1) + t;
+      const bf16x4 ov = {static_cast<bf16>(acc[i][4 * t] * inv), static_cast<bf16>(acc[i][4 * t + 1] * inv),
+                         static_cast<bf16>(acc[i][4 * t + 2] * inv), static_cast<bf16>(acc[i][4 * t + 3] * inv)};
+      const int d = out_block<kDH>(db) - kHalfDims * kp + 8 * g + 4 * half;  // dim within the half
+      *reinterpret_cast<bf16x4*>(tile + l32 * kStride + 2 * d) = ov;
+    }
+  }
+  __syncthreads();
+  const int b = udiv(unit, p.div_hkv), kvh = unit - b * p.Hkv;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int id = int(threadIdx.x) + 64 * kPieces * q, r = id / kChunks, c = id % kChunks;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * kStride + 16 * c);
+    const int rr = row0 + r;
+    if (rr >= p.rows) continue;
+    const int u = idiv(rr, p.rcp_group);
+    const int h = kvh * p.group + (rr - u * p.group);
+    bf16* o = static_cast<bf16*>(p.out) + ((int64_t(b) * p.N + u) * p.Hq + h) * kDH + kHalfDims * kp + 8 * c;
+    *reinterpret_cast<u32x4*>(o) = v;
+  }
 }
+
 
 }  // namespace
 
@@ -1254,7 +1280,7 @@ medusa_status run_mfma(AttnArgs& a, int32_t d_h, hipStream_t stream, void* ev_st
   if (st != MEDUSA_OK) return st;
   MergeArgs m{};
   m.ml = static_cast<const float4*>(a.workspace);
-  m.o = reinterpret_cast<const int16_t*>(static_cast<const unsigned char*>(a.workspace) + plan.o_offset);
+  m.o = static_cast<const unsigned char*>(a.workspace) + plan.o_offset;
   m.out = a.out;
   m.status = a.status;
   m.Hq = a.Hq;
@@ -1272,9 +1298,10 @@ medusa_status run_mfma(AttnArgs& a, int32_t d_h, hipStream_t stream, void* ev_st
                                : reinterpret_cast<const void*>(&tree_attn_merge_kernel<8, kD>))
            : (plan.splits <= 4 ? reinterpret_cast<const void*>(&tree_attn_merge_kernel<4, kD / 2>)
                                : reinterpret_cast<const void*>(&tree_attn_merge_kernel<8, kD / 2>));
-  const int mrows = full ? merge_rows<kD>() : merge_rows<kD / 2>();
-  return launch(merge, dim3(unsigned(plan.units), unsigned(plan.qblocks), unsigned((plan.qrows + mrows - 1) / mrows)),
-                dim3(256), 0, stream, m, nullptr, ev_stop);
+  static_assert(kRowsWave * kWaves / kKeyPhases == 4 * kRowsWave && kKeyPhases == 2,
+                "one merge block per attention wavefront: 4 row blocks x 2 key phases");
+  return launch(merge, dim3(unsigned(plan.units), unsigned(plan.qblocks), unsigned(2 * (plan.qrows / kRowsWave))),
+                dim3(unsigned(64 * (d_h / 32))), 0, stream, m, nullptr, ev_stop);
 }
 
 }  // namespace medusa
