@@ -74,6 +74,15 @@ EDGE = {
     "mfma_group5_d64": (dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=10, Hkv=2, d=64),
                         [1234, 640]),
     "mfma_group7": (dataclasses.replace(workloads.WORKLOADS["batched"], B=1, Hq=7, Hkv=1), [3000]),
+    # matrix-core path with more tree nodes than threads in a workgroup (600: the node depths
+    # are checked and cached in a second pass) and ragged prefixes
+    "mfma_600_nodes": (dataclasses.replace(workloads.WORKLOADS["batched"], B=2, Hq=2, Hkv=1, n_nodes=600,
+                                           use_logits=False, vocab=16), [100, 333]),
+    # matrix-core path with more tree rows than the LDS depth cache holds (4161 > 4096: the
+    # staged-row fixes read the depths from memory), 66 visibility words per row
+    "mfma_4161_rows": (dataclasses.replace(workloads.WORKLOADS["batched"], B=1, Hq=1, Hkv=1, tree="cartesian",
+                                           branching=(64, 64), num_heads=2, topk=64, use_logits=False,
+                                           vocab=128), [77]),
     # a chain: ordinary causal attention over prefix + path
     "chain_f32": (dataclasses.replace(workloads.WORKLOADS["tiny"], Hq=2, Hkv=1, d=128,
                                       branching=(1, 1, 1, 1), num_heads=4, topk=1), [65]),
